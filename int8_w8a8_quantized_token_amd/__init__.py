@@ -1,0 +1,1 @@
+"""MI355X-native W8A8 INT8 linear layer (gfx950)."""

@@ -1,0 +1,285 @@
+"""Reference oracle for the W8A8 INT8 linear layer.
+
+TEST INFRASTRUCTURE ONLY. This is the plain, slow, step-by-step CPU statement
+of what the layer computes. Only the tests, the package smoke check and the
+benchmark's CPU-baseline leg may import it. The GPU library never calls it,
+and it shares no code, table or constant with the GPU library.
+
+Sources, cited by page title and section:
+
+  [HALF]  "Understanding W8A8 INT8 LLM quantization: Half the size, better
+          performance, same accuracy" (Red Hat, part 1 of the series)
+  [PERF]  "Understanding W8A8 INT8 LLM quantization: Accuracy and performance
+          results" (Red Hat, part 2)
+  [PTQ]   "INT8 Post-Training Quantization for LLM Inference on NVIDIA GPUs"
+
+What the layer computes (per linear, at inference):
+
+  1. smooth:   x'[m,j] = x[m,j] / s[j]                        (SmoothQuant)
+  2. scale:    S[m]    = max_j |x'[m,j]| / 127                (per token)
+  3. quantize: q[m,j]  = clamp(round(x'[m,j] / S[m]), -127, 127)
+  4. GEMM:     acc[m,n] = sum_j q[m,j] * Wq[n,j]               (exact integer)
+  5. epilogue: y[m,n]  = bf16(acc[m,n] * S[m] * sw[n])
+
+with offline weight preparation
+
+  0. s[j] = sqrt(max_m |Xcal[m,j]| / max_n |W[n,j]|)            (alpha = 1/2)
+     W'[n,j] = bf16(W[n,j] * s[j]);  sw[n] = max_j |W'[n,j]| / 127
+     Wq[n,j] = clamp(round(W'[n,j] / sw[n]), -127, 127)
+
+Precision and rounding (the readings taken where the pages leave it open):
+
+  * Every floating-point step whose result decides an integer code (steps 0-3)
+    is done in IEEE binary32, one correctly rounded operation at a time,
+    in the order written above. Divisions are true divisions.
+  * round() rounds half away from zero. [HALF] "How SmoothQuant prevents
+    outliers in activation tensors" rounds 0.75/0.012 = 62.5 to 63, and its
+    1.53/0.012 = 127.5 ends at 127, which is what half-away-then-clamp gives.
+  * The clamp keeps codes in [-127, 127]; -128 is never produced.
+  * A token (or weight channel) whose absmax is 0 gets scale 0 and all-zero
+    codes (the pages do not say; this avoids 0/0).
+  * Step 4 is exact: the float64 matmul below only ever holds integers of
+    magnitude <= 128*128*K < 2**53, so every product and partial sum is exact
+    whatever order the library uses.
+  * Step 5 is evaluated in binary64 (the value acc*S*sw carries a relative
+    error of at most 2**-53) and rounded once to bf16, round-to-nearest-even.
+  * bf16 values are handled as their uint16 bit patterns.
+
+Parity pins: every function here is checked in tests/test_oracle_pins.py
+against the pages' worked examples (tests/golden/), closed forms, brute force
+with Python integers and fractions, and invariants of the method.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+QMAX = 127  # largest code; [HALF] "How we compressed the model"
+F32 = np.float32
+
+
+# ---------------------------------------------------------------------------
+# bf16 helpers
+# ---------------------------------------------------------------------------
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> float32. Exact: bf16 is the top half of binary32."""
+    bits = np.asarray(bits, dtype=np.uint16)
+    return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def round_to_bf16(v) -> np.ndarray:
+    """Round real values (float64 or float32 arrays) once to bf16,
+    round-to-nearest-even. Returns uint16 bit patterns.
+
+    bf16 keeps 8 significant bits and binary32's exponent range. A value is
+    scaled by a power of two so that its rounding quantum becomes 1, rounded
+    with rint (ties to even), and scaled back; all scalings are exact.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    out = np.zeros(v.shape, dtype=np.float64)
+    nz = v != 0
+    _, e = np.frexp(v[nz])                       # |v| = f * 2**e, f in [0.5, 1)
+    qexp = np.maximum(e - 8, -133)               # 8 significant bits; subnormal floor
+    r = np.rint(np.ldexp(v[nz], -qexp))          # integer count of quanta
+    out[nz] = np.ldexp(r, qexp)
+    big = np.abs(out) > float(np.ldexp(255.0 / 128.0, 127))   # beyond bf16 max
+    out[big] = np.copysign(np.inf, out[big])
+    out = np.where(nz, out, v)                   # keep the sign of zero
+    return (out.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+# ---------------------------------------------------------------------------
+# rounding to int8 codes
+# ---------------------------------------------------------------------------
+
+def round_half_away(v: np.ndarray) -> np.ndarray:
+    """Nearest integer, ties away from zero, for float32 values (exact).
+
+    trunc(v) and v - trunc(v) are both exact in binary32, so the comparison
+    of the discarded fraction with 1/2 is exact.
+    """
+    v = np.asarray(v, dtype=F32)
+    t = np.trunc(v)
+    frac = v - t
+    up = np.abs(frac) >= F32(0.5)
+    return (t.astype(np.int64) + np.where(up, np.sign(v).astype(np.int64), 0))
+
+
+def quantize_with_scale(xs: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """q = clamp(round(x / S), -127, 127) in binary32; S == 0 gives q = 0.
+
+    [HALF] "The problem with naive quantization" (scale and round),
+    [HALF] "How SmoothQuant prevents outliers in activation tensors" (ties),
+    [PTQ] "1. Min-Max Calibration" (the symmetric [-127, 127] range).
+    ``scale`` broadcasts against ``xs`` (one scale per row here).
+    """
+    xs = np.asarray(xs, dtype=F32)
+    scale = np.asarray(scale, dtype=F32)
+    safe = np.where(scale == 0, F32(1), scale)
+    with np.errstate(over="ignore"):
+        v = xs / safe
+    # saturate before rounding (a fixed scale can send x/S past int range);
+    # every |v| >= 127.5 ends at +-127 either way
+    v = np.clip(v, F32(-2 * QMAX), F32(2 * QMAX))
+    q = np.clip(round_half_away(v), -QMAX, QMAX)
+    q = np.where(scale == 0, 0, q)
+    return q.astype(np.int8)
+
+
+def absmax_scale(xs: np.ndarray, axis: int = -1) -> np.ndarray:
+    """S = max|x| / 127 along ``axis`` (binary32 division).
+
+    [HALF] "How we compressed the model" (scale from the largest magnitude),
+    [HALF] "Why activation quantization is hard" (one scale per token).
+    """
+    a = np.max(np.abs(np.asarray(xs, dtype=F32)), axis=axis)
+    return (a / F32(QMAX)).astype(F32)
+
+
+# ---------------------------------------------------------------------------
+# steps 1-3: per-token dynamic activation quantization
+# ---------------------------------------------------------------------------
+
+def smooth_activations(x32: np.ndarray, smooth) -> np.ndarray:
+    """x' = x / s (binary32 division per element). ``smooth`` None: x' = x.
+
+    [HALF] "How the SmoothQuant smoothing factor is computed": each channel
+    is divided by its factor (folded into RMSNorm's gamma there; applied to
+    the activation here).
+    """
+    x32 = np.asarray(x32, dtype=F32)
+    if smooth is None:
+        return x32.copy()
+    smooth = np.asarray(smooth, dtype=F32)
+    assert np.all(smooth > 0) and np.all(np.isfinite(smooth)), "smooth must be > 0"
+    return x32 / smooth[None, :]
+
+
+def quantize_act_f32(x32: np.ndarray, smooth=None):
+    """Per-token dynamic quantization of float32 activations [M, K].
+
+    Returns (q int8 [M, K], S float32 [M]).
+    [HALF] "Why activation quantization is hard, and how SmoothQuant fixes it";
+    [PERF] "Inter-token latency (ITL)" (range, scale, convert, per token).
+    """
+    x32 = np.asarray(x32, dtype=F32)
+    assert x32.ndim == 2 and np.all(np.isfinite(x32)), "finite [M, K] input"
+    xs = smooth_activations(x32, smooth)
+    s_tok = absmax_scale(xs, axis=1)
+    q = quantize_with_scale(xs, s_tok[:, None])
+    return q, s_tok
+
+
+def quantize_act(x_bf16: np.ndarray, smooth=None):
+    """quantize_act_f32 on bf16 activations given as uint16 bit patterns."""
+    return quantize_act_f32(bf16_to_f32(x_bf16), smooth)
+
+
+# ---------------------------------------------------------------------------
+# step 0: offline preparation (smoothing factors, weight quantization)
+# ---------------------------------------------------------------------------
+
+def act_channel_absmax(x_bf16: np.ndarray) -> np.ndarray:
+    """max over tokens of |X[m, j]| for every input channel j (float32 [K])."""
+    return np.max(np.abs(bf16_to_f32(x_bf16)), axis=0).astype(F32)
+
+
+def weight_channel_absmax(w_bf16: np.ndarray) -> np.ndarray:
+    """max over output channels of |W[n, j]| for every input channel j.
+
+    W is stored [N, K]; the page's K x N example calls this "row j of the
+    receiving layer's weight" ([HALF] "How the SmoothQuant smoothing factor
+    is computed").
+    """
+    return np.max(np.abs(bf16_to_f32(w_bf16)), axis=0).astype(F32)
+
+
+def smoothing_factors(act_absmax: np.ndarray, w_absmax: np.ndarray) -> np.ndarray:
+    """s[j] = sqrt(act_absmax[j] / w_absmax[j]) in binary32; 1 where either is 0.
+
+    SmoothQuant's factor with migration strength alpha = 1/2; the page lists
+    its terms ([HALF] "How the SmoothQuant smoothing factor is computed") and
+    uses alpha = 0.8 there; the square root is the alpha = 1/2 member.
+    """
+    a = np.asarray(act_absmax, dtype=F32)
+    w = np.asarray(w_absmax, dtype=F32)
+    ok = (a > 0) & (w > 0)
+    ratio = np.where(ok, a / np.where(ok, w, F32(1)), F32(1))
+    return np.where(ok, np.sqrt(ratio.astype(F32)), F32(1)).astype(F32)
+
+
+def smooth_weight(w_bf16: np.ndarray, smooth) -> np.ndarray:
+    """W'[n, j] = bf16(W[n, j] * s[j]): binary32 product, then bf16 (RNE).
+
+    The weights stay bf16 after smoothing ([HALF] "How the SmoothQuant
+    smoothing factor is computed").
+    """
+    w32 = bf16_to_f32(w_bf16)
+    if smooth is None:
+        return np.asarray(w_bf16, dtype=np.uint16).copy()
+    prod = w32 * np.asarray(smooth, dtype=F32)[None, :]
+    return round_to_bf16(prod)
+
+
+def quantize_weight_f32(w32: np.ndarray):
+    """Per-output-channel symmetric RTN of float32 weights [N, K].
+
+    Returns (Wq int8 [N, K], sw float32 [N]).
+    [HALF] "The problem with naive quantization": one scale per weight
+    channel (a column of its K x N example = a row of our [N, K] layout).
+    """
+    w32 = np.asarray(w32, dtype=F32)
+    sw = absmax_scale(w32, axis=1)
+    return quantize_with_scale(w32, sw[:, None]), sw
+
+
+def quantize_weight(w_bf16: np.ndarray):
+    return quantize_weight_f32(bf16_to_f32(w_bf16))
+
+
+def prepare_weight(w_bf16: np.ndarray, smooth):
+    """Smooth then quantize: (Wq int8 [N, K], sw float32 [N])."""
+    return quantize_weight(smooth_weight(w_bf16, smooth))
+
+
+# ---------------------------------------------------------------------------
+# steps 4-5: integer GEMM and dequantizing epilogue
+# ---------------------------------------------------------------------------
+
+def gemm_i32(xq: np.ndarray, wq: np.ndarray) -> np.ndarray:
+    """acc[m, n] = sum_k xq[m, k] * wq[n, k], exact; returned as int32.
+
+    [HALF] "How we compressed the model" (both operands int8 in the matmul).
+    """
+    xq = np.asarray(xq, dtype=np.int8)
+    wq = np.asarray(wq, dtype=np.int8)
+    assert xq.ndim == 2 and wq.ndim == 2 and xq.shape[1] == wq.shape[1]
+    K = xq.shape[1]
+    assert 128 * 128 * max(K, 1) < 2 ** 53
+    acc = xq.astype(np.float64) @ wq.astype(np.float64).T
+    acc_i = acc.astype(np.int64)
+    assert np.all(acc_i == acc)
+    assert np.all(np.abs(acc_i) < 2 ** 31), "accumulator leaves int32"
+    return acc_i.astype(np.int32)
+
+
+def dequant_epilogue(acc: np.ndarray, s_tok: np.ndarray, s_chan: np.ndarray):
+    """y[m, n] = acc[m, n] * S[m] * sw[n] in binary64, then once to bf16.
+
+    The per-token and per-channel scales factor out of the K-sum, so they are
+    applied after accumulation ([HALF] "Why activation quantization is hard";
+    [PERF] "Inter-token latency (ITL)": convert back to BF16).
+    Returns (y float64 [M, N], y bf16 bits uint16 [M, N]).
+    """
+    y = (np.asarray(acc, dtype=np.float64)
+         * np.asarray(s_tok, dtype=F32).astype(np.float64)[:, None]
+         * np.asarray(s_chan, dtype=F32).astype(np.float64)[None, :])
+    return y, round_to_bf16(y)
+
+
+def linear(x_bf16: np.ndarray, smooth, wq: np.ndarray, s_chan: np.ndarray):
+    """Steps 1-5 for one linear. Returns a dict of every intermediate."""
+    xq, s_tok = quantize_act(x_bf16, smooth)
+    acc = gemm_i32(xq, wq)
+    y64, y = dequant_epilogue(acc, s_tok, s_chan)
+    return {"xq": xq, "s_tok": s_tok, "acc": acc, "y64": y64, "y": y}

@@ -1,0 +1,130 @@
+"""The oracle's pins must catch plausible mistakes.
+
+Each case plants one mistake in the oracle (on the CPU, by monkeypatching a
+function of oracle.w8a8_oracle) and runs the pin tests; at least one pin must
+fail. The oracle itself is restored after every case.
+"""
+import numpy as np
+import pytest
+
+import test_oracle_pins as P
+from oracle import w8a8_oracle as O
+
+F32 = np.float32
+
+
+def _rint_round(v):                           # ties to even instead of away
+    return np.rint(np.asarray(v, dtype=F32)).astype(np.int64)
+
+
+def _ceil_ties(v):                            # ties toward +inf (sign slip)
+    return np.floor(np.asarray(v, dtype=np.float64) + 0.5).astype(np.int64)
+
+
+def _no_clamp(xs, scale):
+    xs = np.asarray(xs, dtype=F32)
+    scale = np.asarray(scale, dtype=F32)
+    safe = np.where(scale == 0, F32(1), scale)
+    v = np.clip(xs / safe, F32(-1e6), F32(1e6))
+    q = O.round_half_away(v)
+    q = np.where(scale == 0, 0, q)
+    return q.astype(np.int64).astype(np.int8)      # wraps 128 to -128
+
+
+def _recip_mul(xs, scale):                    # x * (1/S) instead of x / S
+    xs = np.asarray(xs, dtype=F32)
+    scale = np.asarray(scale, dtype=F32)
+    safe = np.where(scale == 0, F32(1), scale)
+    v = np.clip(xs * (F32(1) / safe), F32(-254), F32(254))
+    q = np.clip(O.round_half_away(v), -127, 127)
+    return np.where(scale == 0, 0, q).astype(np.int8)
+
+
+def _signed_max_scale(xs, axis=-1):           # max instead of max |x|
+    return (np.max(np.asarray(xs, dtype=F32), axis=axis) / F32(127)).astype(F32)
+
+
+def _scale_128(xs, axis=-1):
+    return (np.max(np.abs(np.asarray(xs, dtype=F32)), axis=axis) / F32(128)).astype(F32)
+
+
+def _smooth_mul(x32, smooth):                 # multiply instead of divide
+    x32 = np.asarray(x32, dtype=F32)
+    return x32.copy() if smooth is None else x32 * np.asarray(smooth, dtype=F32)[None, :]
+
+
+def _gemm_no_transpose(xq, wq):
+    return (np.asarray(xq, np.int64) @ np.asarray(wq, np.int64)).astype(np.int32)
+
+
+def _gemm_wrong_operand(xq, wq):              # W^T X^T: transposed result
+    return (np.asarray(wq, np.int64) @ np.asarray(xq, np.int64).T).T.copy().astype(np.int32)[:, ::-1]
+
+
+def _epilogue_swapped(acc, s_tok, s_chan):
+    M, N = np.asarray(acc).shape
+    st = np.resize(np.asarray(s_chan, F32), M)
+    sc = np.resize(np.asarray(s_tok, F32), N)
+    y = np.asarray(acc, np.float64) * st.astype(np.float64)[:, None] * sc.astype(np.float64)[None, :]
+    return y, O.round_to_bf16(y)
+
+
+def _bf16_truncate(v):
+    v = np.asarray(v, dtype=np.float64).astype(F32)
+    return (v.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def _smoothing_alpha1(a, w):
+    a = np.asarray(a, F32)
+    w = np.asarray(w, F32)
+    ok = (a > 0) & (w > 0)
+    return np.where(ok, a / np.where(ok, w, F32(1)), F32(1)).astype(F32)
+
+
+def _smoothing_inverted(a, w):
+    return O.smoothing_factors(w, a)
+
+
+def _smooth_weight_div(w_bf16, smooth):
+    return O.round_to_bf16(O.bf16_to_f32(w_bf16) / np.asarray(smooth, F32)[None, :])
+
+
+def _quantize_weight_per_input(w32):
+    w32 = np.asarray(w32, dtype=F32)
+    sw = O.absmax_scale(w32, axis=0)
+    return O.quantize_with_scale(w32, sw[None, :]), sw
+
+
+MUTANTS = {
+    "ties_to_even": ("round_half_away", _rint_round),
+    "ties_toward_plus_inf": ("round_half_away", _ceil_ties),
+    "no_clamp": ("quantize_with_scale", _no_clamp),
+    "reciprocal_multiply": ("quantize_with_scale", _recip_mul),
+    "signed_max_scale": ("absmax_scale", _signed_max_scale),
+    "scale_over_128": ("absmax_scale", _scale_128),
+    "smooth_multiplies": ("smooth_activations", _smooth_mul),
+    "gemm_no_transpose": ("gemm_i32", _gemm_no_transpose),
+    "gemm_wrong_orientation": ("gemm_i32", _gemm_wrong_operand),
+    "epilogue_scales_swapped": ("dequant_epilogue", _epilogue_swapped),
+    "bf16_truncates": ("round_to_bf16", _bf16_truncate),
+    "smoothing_alpha_one": ("smoothing_factors", _smoothing_alpha1),
+    "smoothing_inverted": ("smoothing_factors", _smoothing_inverted),
+    "smooth_weight_divides": ("smooth_weight", _smooth_weight_div),
+    "weight_scale_per_input_channel": ("quantize_weight_f32", _quantize_weight_per_input),
+}
+
+PINS = [getattr(P, n) for n in dir(P)
+        if n.startswith("test_") and callable(getattr(P, n))]
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_some_pin_catches(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(O, attr, fn)
+    caught = []
+    for pin in PINS:
+        try:
+            pin()
+        except Exception:                         # assertion or shape error
+            caught.append(pin.__name__)
+    assert caught, f"mutant {name} survived every pin"

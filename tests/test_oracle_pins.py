@@ -1,0 +1,416 @@
+"""Pins for the CPU oracle: page worked examples, exact brute force with
+Python integers and fractions, closed forms and invariants of the method.
+
+None of these checks re-types the oracle's own formulas in numpy: the brute
+force below rounds exact rationals to binary32/bf16 with integer arithmetic,
+so a wrong division order, tie rule, clamp, operand orientation, scale index
+or bf16 rounding in the oracle fails at least one of them.
+"""
+import json
+import math
+import os
+from decimal import Decimal, getcontext
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from conftest import GOLDEN
+from oracle import w8a8_oracle as O
+
+F32 = np.float32
+
+
+def golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------------------
+# exact reference arithmetic (independent of numpy's float ops)
+# ---------------------------------------------------------------------------
+
+def rn(fr: Fraction, p: int, emin: int = -126) -> Fraction:
+    """Round a rational to the nearest p-bit binary float, ties to even."""
+    if fr == 0:
+        return Fraction(0)
+    sign = -1 if fr < 0 else 1
+    a = abs(fr)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    qe = max(e - (p - 1), emin - (p - 1))
+    scaled = a / Fraction(2) ** qe
+    n = scaled.numerator // scaled.denominator
+    rem = scaled - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    return sign * n * Fraction(2) ** qe
+
+
+def rn32(fr):
+    return rn(fr, 24)
+
+
+def rnbf16(fr):
+    return rn(fr, 8)
+
+
+def half_away(fr: Fraction) -> int:
+    s = -1 if fr < 0 else 1
+    a = abs(fr)
+    return s * int(math.floor(a + Fraction(1, 2)))
+
+
+def bf16_bits_of(fr: Fraction) -> int:
+    v = np.float32(float(fr))          # fr is a bf16 value: exact in float32
+    assert Fraction(float(v)) == fr
+    return int(np.array([v], dtype=F32).view(np.uint32)[0] >> 16)
+
+
+def ref_quantize_row(x, s=None):
+    """Brute-force per-token quantization of one row given as float32s."""
+    xs = [rn32(Fraction(float(v)) / Fraction(float(sj))) if s is not None else Fraction(float(v))
+          for v, sj in zip(x, s if s is not None else [1] * len(x))]
+    a = max(abs(v) for v in xs)
+    S = rn32(a / 127)
+    if S == 0:
+        return [0] * len(xs), S
+    q = [max(-127, min(127, half_away(rn32(v / S)))) for v in xs]
+    return q, S
+
+
+# ---------------------------------------------------------------------------
+# page worked examples
+# ---------------------------------------------------------------------------
+
+def test_page_weight_rtn_example():
+    g = golden("half_weight_rtn.json")
+    w_kn = np.array(g["W_KxN"], dtype=F32)
+    wq, sw = O.quantize_weight_f32(w_kn.T)            # our layout is [N, K]
+    np.testing.assert_allclose(sw, g["scales_printed"], atol=5e-7)
+    np.testing.assert_array_equal(wq.T, np.array(g["q_arith_KxN"]))
+    # the printed 62 differs only in that entry, and the page's own
+    # reconstruction uses it: 62 * 0.007323 = 0.4540
+    qp = np.array(g["q_printed_KxN"])
+    assert (qp != wq.T).sum() == 1
+    recon_page = qp * np.array(g["scales_printed"])[None, :]
+    np.testing.assert_allclose(recon_page, g["recon_printed_KxN"], atol=g["tol_printed"])
+    # reconstruction of our codes matches the page wherever the codes agree
+    recon = wq.T.astype(np.float64) * sw.astype(np.float64)[None, :]
+    agree = qp == wq.T
+    np.testing.assert_allclose(recon[agree], np.array(g["recon_printed_KxN"])[agree], atol=1e-4)
+    x = np.array(g["x"])
+    np.testing.assert_allclose(x @ w_kn.astype(np.float64), g["y_original_printed"], atol=g["tol_printed"])
+    np.testing.assert_allclose(x @ recon_page, g["y_recon_printed"], atol=g["tol_printed"])
+    np.testing.assert_allclose(x @ recon, g["y_recon_arith"], atol=g["tol_printed"])
+
+
+def test_page_activation_outlier_example():
+    g = golden("half_activation_outlier.json")
+    q, S = O.quantize_act_f32(np.array([g["x"]], dtype=F32))
+    assert abs(float(S[0]) - g["scale_printed"]) < g["scale_tol"]
+    assert q[0].tolist() == g["q_printed"]
+
+
+def test_page_smoothquant_gamma_example():
+    g = golden("half_smoothquant_gamma.json")
+    act = np.array(g["normalized"], dtype=F32) * np.array(g["gamma"], dtype=F32)
+    np.testing.assert_array_equal(act, np.array(g["activation_printed"], dtype=F32))
+    smooth = np.array(g["smooth"], dtype=F32)
+    xs = O.smooth_activations(act[None, :], smooth)
+    np.testing.assert_array_equal(xs[0], np.array(g["smoothed_printed"], dtype=F32))
+    # the page's fixed scale: exact ties 62.5 and 127.5 -> 63 and 127
+    q_fixed = O.quantize_with_scale(xs, F32(g["scale_printed"]))
+    assert q_fixed[0].tolist() == g["q_printed_at_scale_printed"]
+    # dynamic per-token scale
+    q, S = O.quantize_act_f32(act[None, :], smooth)
+    assert q[0].tolist() == g["q_dynamic"]
+    assert abs(float(S[0]) - 1.53 / 127) < 1e-8
+    # without smoothing the three small channels collapse (outlier example)
+    q0, _ = O.quantize_act_f32(act[None, :])
+    assert q0[0].tolist() == [1, 1, 1, 127]
+
+
+# ---------------------------------------------------------------------------
+# rounding rule and clamp
+# ---------------------------------------------------------------------------
+
+def test_round_half_away_vs_fraction():
+    r = np.random.default_rng(1)
+    v = np.concatenate([
+        (r.integers(-260, 260, 4000) + 0.5).astype(F32),               # exact ties
+        r.uniform(-130, 130, 20000).astype(F32),
+        np.array([0.0, -0.0, 0.49999997, -0.49999997, 0.5, -0.5, 1.5, 2.5, -2.5,
+                  126.5, 127.49999, 127.5, -127.5, 1e-30, -1e-30], dtype=F32)])
+    got = O.round_half_away(v)
+    want = [half_away(Fraction(float(x))) for x in v]
+    np.testing.assert_array_equal(got, want)
+
+
+def test_crafted_ties_dynamic_scale_is_power_of_two():
+    # row max 127 * 2**k makes S = 2**k exactly, so (n + 1/2) * 2**k are ties
+    for k in (-10, 0, 3):
+        row = np.array([127, 62.5, -62.5, 0.5, -0.5, 1.5, -1.5, 126.5, -126.5, 0.25],
+                       dtype=F32) * F32(2.0 ** k)
+        q, S = O.quantize_act_f32(row[None, :])
+        assert float(S[0]) == 2.0 ** k
+        assert q[0].tolist() == [127, 63, -63, 1, -1, 2, -2, 127, -127, 0]
+
+
+def test_fixed_scale_clamps_and_saturates():
+    xs = np.array([[1e30, -1e30, 200.0, -200.0, 127.4, 127.5, -127.5]], dtype=F32)
+    q = O.quantize_with_scale(xs, F32(1.0))
+    assert q[0].tolist() == [127, -127, 127, -127, 127, 127, -127]
+    assert O.quantize_with_scale(xs, F32(0.0))[0].tolist() == [0] * 7
+
+
+# ---------------------------------------------------------------------------
+# activation quantization: brute force + invariants
+# ---------------------------------------------------------------------------
+
+def test_quantize_act_vs_fraction_brute_force():
+    r = np.random.default_rng(2)
+    for trial in range(40):
+        K = int(r.integers(1, 24))
+        x = r.standard_normal(K).astype(F32) * F32(10.0 ** r.integers(-3, 3))
+        if trial % 3 == 0:
+            x[r.integers(0, K)] *= F32(20)
+        s = np.exp(r.uniform(-2, 2, K)).astype(F32) if trial % 2 else None
+        q, S = O.quantize_act_f32(x[None, :], s)
+        qref, Sref = ref_quantize_row(x, s)
+        assert Fraction(float(S[0])) == Sref
+        assert q[0].tolist() == qref, (trial, x, s)
+
+
+def test_quantize_act_invariants():
+    r = np.random.default_rng(3)
+    M, K = 64, 512
+    x = r.standard_normal((M, K)).astype(F32)
+    x[:, r.choice(K, 5, replace=False)] *= F32(20)
+    x[7] = 0.0                                            # zero row
+    x[9, :] = F32(1e-39)                                  # subnormal row
+    s = np.exp(r.uniform(-1, 1, K)).astype(F32)
+    q, S = O.quantize_act_f32(x, s)
+    xs = (x / s[None, :]).astype(F32)
+    assert q.dtype == np.int8 and q.min() >= -127
+    nz = np.any(xs != 0, axis=1)
+    assert S[7] == 0 and np.all(q[7] == 0)
+    # every nonzero row reaches +-127 exactly once its max is scaled
+    assert np.all(np.max(np.abs(q[nz].astype(int)), axis=1) == 127)
+    # dequantize(quantize(x)) is within S/2 (plus binary32 slack)
+    err = np.abs(q.astype(np.float64) * S[:, None].astype(np.float64) - xs.astype(np.float64))
+    assert np.all(err <= S[:, None].astype(np.float64) * 0.5 * (1 + 2.0 ** -20))
+    # sign agreement and monotonicity within each row
+    assert np.all((np.sign(q) == np.sign(xs)) | (q == 0))
+    for m in range(0, M, 7):
+        order = np.argsort(xs[m], kind="stable")
+        assert np.all(np.diff(q[m][order].astype(int)) >= 0)
+    # scaling a row by a power of two scales S and keeps q
+    q2, S2 = O.quantize_act_f32(x * F32(8.0), s)
+    np.testing.assert_array_equal(q2[nz], q[nz])
+    np.testing.assert_array_equal(S2[nz & (S > 1e-30)], S[nz & (S > 1e-30)] * F32(8.0))
+    # rows are independent
+    qs, Ss = O.quantize_act_f32(x[10:20], s)
+    np.testing.assert_array_equal(qs, q[10:20])
+    np.testing.assert_array_equal(Ss, S[10:20])
+
+
+def test_quantize_act_bf16_wrapper():
+    bits = np.array([[0x3F80, 0xBF80, 0x4000, 0x0000]], dtype=np.uint16)   # 1, -1, 2, 0
+    q, S = O.quantize_act(bits)
+    assert float(S[0]) == np.float32(2.0) / np.float32(127)
+    assert q[0].tolist() == [64, -64, 127, 0]    # 63.5 -> 64 (half away)
+
+
+# ---------------------------------------------------------------------------
+# GEMM
+# ---------------------------------------------------------------------------
+
+def test_gemm_vs_python_ints():
+    r = np.random.default_rng(4)
+    for (M, N, K) in [(1, 1, 1), (3, 5, 7), (17, 9, 33), (2, 31, 64)]:
+        a = r.integers(-127, 128, (M, K)).astype(np.int8)
+        b = r.integers(-127, 128, (N, K)).astype(np.int8)
+        got = O.gemm_i32(a, b)
+        want = [[sum(int(a[m, k]) * int(b[n, k]) for k in range(K)) for n in range(N)]
+                for m in range(M)]
+        np.testing.assert_array_equal(got, want)
+        assert got.shape == (M, N)
+
+
+def test_gemm_closed_forms():
+    K = 28672
+    a = np.full((2, K), 127, np.int8)
+    b = np.stack([np.full(K, 127, np.int8), np.full(K, -127, np.int8)])
+    acc = O.gemm_i32(a, b)
+    assert acc.tolist() == [[16129 * K, -16129 * K]] * 2
+    # one-hot weight rows pick columns of the activation codes
+    r = np.random.default_rng(5)
+    x = r.integers(-127, 128, (6, 40)).astype(np.int8)
+    idx = [3, 0, 39, 17]
+    w = np.zeros((4, 40), np.int8)
+    w[np.arange(4), idx] = 1
+    np.testing.assert_array_equal(O.gemm_i32(x, w), x[:, idx].astype(np.int32))
+
+
+# ---------------------------------------------------------------------------
+# epilogue and bf16 rounding
+# ---------------------------------------------------------------------------
+
+def test_round_to_bf16_known_cases():
+    cases = {1 + 2 ** -8: 0x3F80,                 # tie -> even (1.0)
+             1 + 3 * 2 ** -8: 0x3F82,             # tie -> even (1 + 2**-6)
+             1 + 2 ** -8 + 2 ** -30: 0x3F81,      # just above the tie
+             -(1 + 2 ** -8): 0xBF80,
+             2.0 ** -133: 0x0001,                 # smallest subnormal
+             3.4e38: 0x7F80,                      # rounds past bf16 max -> inf
+             0.0: 0x0000}
+    got = O.round_to_bf16(np.array(list(cases.keys())))
+    assert got.tolist() == list(cases.values())
+
+
+def test_epilogue_vs_fraction():
+    r = np.random.default_rng(6)
+    M, N = 5, 7
+    acc = r.integers(-2 ** 28, 2 ** 28, (M, N)).astype(np.int32)
+    acc[0, 0] = 0
+    s_tok = (r.uniform(1e-4, 1e-1, M)).astype(F32)
+    s_chan = (r.uniform(1e-5, 1e-2, N)).astype(F32)
+    y64, y = O.dequant_epilogue(acc, s_tok, s_chan)
+    for m in range(M):
+        for n in range(N):
+            exact = Fraction(int(acc[m, n])) * Fraction(float(s_tok[m])) * Fraction(float(s_chan[n]))
+            assert int(y[m, n]) == bf16_bits_of(rnbf16(exact))
+            assert abs(Fraction(float(y64[m, n])) - exact) <= abs(exact) * Fraction(1, 2 ** 52)
+    assert int(y[0, 0]) == 0
+
+
+def test_epilogue_scale_orientation():
+    acc = np.array([[257, 259], [256, -257]], dtype=np.int32)
+    s_tok = np.array([2.0 ** -8, 2.0 ** -7], dtype=F32)
+    s_chan = np.array([1.0, 2.0], dtype=F32)
+    _, y = O.dequant_epilogue(acc, s_tok, s_chan)
+    # y = acc * s_tok[m] * s_chan[n]
+    assert y.tolist() == [[0x3F80, 0x4002], [0x4000, 0xC080]]
+
+
+# ---------------------------------------------------------------------------
+# smoothing factors and weight preparation
+# ---------------------------------------------------------------------------
+
+def _sqrt_rn32(fr: Fraction) -> Fraction:
+    getcontext().prec = 60
+    d = (Decimal(fr.numerator) / Decimal(fr.denominator)).sqrt()
+    return rn32(Fraction(d))
+
+
+def test_smoothing_factors_vs_exact():
+    r = np.random.default_rng(7)
+    ax = np.abs(r.standard_normal(200)).astype(F32) * F32(20)
+    aw = np.abs(r.standard_normal(200)).astype(F32) * F32(0.05)
+    ax[0], aw[1] = 0, 0
+    ax[2], aw[2] = 4.0, 1.0
+    s = O.smoothing_factors(ax, aw)
+    assert s[0] == 1 and s[1] == 1 and s[2] == 2
+    for j in range(3, 200):
+        ratio = rn32(Fraction(float(ax[j])) / Fraction(float(aw[j])))
+        assert Fraction(float(s[j])) == _sqrt_rn32(ratio)
+
+
+def test_smoothing_balances_activation_and_weight_ranges():
+    # alpha = 1/2: after smoothing, a channel's activation absmax and its
+    # weight absmax are both sqrt(ax * aw)
+    r = np.random.default_rng(8)
+    K, M, N = 96, 32, 48
+    out = r.choice(K, 4, replace=False)
+    x = r.standard_normal((M, K)).astype(F32)
+    x[:, out] *= F32(20)
+    w = (r.standard_normal((N, K)) * 0.02).astype(F32)
+    xb, wb = O.round_to_bf16(x), O.round_to_bf16(w)
+    ax, aw = O.act_channel_absmax(xb), O.weight_channel_absmax(wb)
+    s = O.smoothing_factors(ax, aw)
+    x_s = O.smooth_activations(O.bf16_to_f32(xb), s)
+    w_s = O.bf16_to_f32(wb) * s[None, :]
+    target = np.sqrt(ax.astype(np.float64) * aw.astype(np.float64))
+    np.testing.assert_allclose(np.max(np.abs(x_s), axis=0), target, rtol=1e-6)
+    np.testing.assert_allclose(np.max(np.abs(w_s), axis=0), target, rtol=1e-6)
+    # the product is unchanged (before the weight is re-rounded to bf16)
+    xw = O.bf16_to_f32(xb).astype(np.float64) @ O.bf16_to_f32(wb).astype(np.float64).T
+    np.testing.assert_allclose(x_s.astype(np.float64) @ w_s.astype(np.float64).T, xw,
+                               rtol=1e-5, atol=1e-6 * np.abs(xw).max())
+    # smoothing flattens the outlier channels seen by the per-token scale
+    ratio_before = np.max(np.abs(O.bf16_to_f32(xb)), axis=1) / np.median(np.abs(O.bf16_to_f32(xb)), axis=1)
+    ratio_after = np.max(np.abs(x_s), axis=1) / np.median(np.abs(x_s), axis=1)
+    assert np.median(ratio_after) < 0.5 * np.median(ratio_before)
+
+
+def test_smooth_weight_vs_fraction():
+    r = np.random.default_rng(9)
+    w = O.round_to_bf16((r.standard_normal((6, 10)) * 0.02).astype(F32))
+    s = np.exp(r.uniform(-2, 2, 10)).astype(F32)
+    ws = O.smooth_weight(w, s)
+    w32 = O.bf16_to_f32(w)
+    for n in range(6):
+        for j in range(10):
+            prod = rn32(Fraction(float(w32[n, j])) * Fraction(float(s[j])))
+            assert int(ws[n, j]) == bf16_bits_of(rnbf16(prod))
+
+
+def test_quantize_weight_per_output_channel_vs_fraction():
+    r = np.random.default_rng(10)
+    N, K = 7, 19
+    w = O.round_to_bf16((r.standard_normal((N, K)) * 0.02).astype(F32))
+    wq, sw = O.quantize_weight(w)
+    w32 = O.bf16_to_f32(w)
+    for n in range(N):
+        qref, Sref = ref_quantize_row(w32[n])          # one scale per output channel
+        assert Fraction(float(sw[n])) == Sref
+        assert wq[n].tolist() == qref
+
+
+# ---------------------------------------------------------------------------
+# the whole layer
+# ---------------------------------------------------------------------------
+
+def test_linear_matches_brute_force_small():
+    r = np.random.default_rng(11)
+    M, N, K = 3, 4, 16
+    x = O.round_to_bf16(r.standard_normal((M, K)).astype(F32))
+    w = O.round_to_bf16((r.standard_normal((N, K)) * 0.02).astype(F32))
+    s = O.smoothing_factors(O.act_channel_absmax(x), O.weight_channel_absmax(w))
+    wq, sw = O.prepare_weight(w, s)
+    out = O.linear(x, s, wq, sw)
+    x32 = O.bf16_to_f32(x)
+    for m in range(M):
+        qref, Sref = ref_quantize_row(x32[m], s)
+        assert out["xq"][m].tolist() == qref
+        for n in range(N):
+            acc = sum(qref[k] * int(wq[n, k]) for k in range(K))
+            assert int(out["acc"][m, n]) == acc
+            exact = Fraction(acc) * Sref * Fraction(float(sw[n]))
+            assert int(out["y"][m, n]) == bf16_bits_of(rnbf16(exact))
+
+
+def test_w8a8_output_close_to_unquantized_and_smoothing_helps():
+    # sanity (not parity): relative Frobenius error of the W8A8 layer against
+    # the float product, with and without smoothing, on outlier data
+    r = np.random.default_rng(12)
+    M, N, K = 32, 64, 256
+    x = r.standard_normal((M, K)).astype(F32)
+    x[:, r.choice(K, 3, replace=False)] *= F32(30)
+    xb = O.round_to_bf16(x)
+    wb = O.round_to_bf16((r.standard_normal((N, K)) * 0.02).astype(F32))
+    ref = O.bf16_to_f32(xb).astype(np.float64) @ O.bf16_to_f32(wb).astype(np.float64).T
+
+    def rel(smooth):
+        wq, sw = O.prepare_weight(wb, smooth)
+        y = O.linear(xb, smooth, wq, sw)["y64"]
+        return np.linalg.norm(y - ref) / np.linalg.norm(ref)
+
+    s = O.smoothing_factors(O.act_channel_absmax(xb), O.weight_channel_absmax(wb))
+    e_plain, e_smooth = rel(None), rel(s)
+    assert e_smooth < 0.05
+    assert e_smooth < e_plain
