@@ -1,0 +1,304 @@
+#!/usr/bin/env python3
+"""Benchmark of the W8A8 INT8 linear layer on one MI355X (gfx950).
+
+Workload: the Llama-3.1-8B projections (qkv 4096->6144, o 4096->4096,
+gate_up 4096->28672, down 14336->4096) over 32 layers with distinct weight
+buffers (7 GB of int8 weights, far beyond the 256 MB Infinity Cache), on
+seeded synthetic bf16 inputs with 1% outlier channels x20.
+
+  * decode step (the headline `value`): one forward through 32 layers x 4
+    projections at each token count M in {1, 4, 16, 64}; every linear is a
+    w8a8_linear call (quantize + skinny GEMM + epilogue). Metric: algorithmic
+    HBM bytes per second, bytes = 2MK + 4K + NK + 4N + 2MN per linear.
+  * prefill step (reported under "prefill"): the same 128 linears at
+    M = 4096. Metric: int8 TOPS = 2MNK per linear / time.
+
+Each step is captured once in a HIP graph and replayed; W untimed warmup
+steps, then K timed steps between two events on the replay stream.
+The roofline entry times the dominant kernel (the GEMM) alone: a graph of
+the step's GEMM launches only, timed the same way; its average launch
+duration is the graph time over the number of launches.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA, TOPS
+LAYERS = 32
+DECODE_MS = (1, 4, 16, 64)
+PREFILL_M = 4096
+METRIC = "W8A8 GEMM int8 TOPS (prefill) + HBM GB/s (decode), Llama-3.1-8B shapes"
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-cpu-baseline", action="store_true",
+                   help="skip timing the CPU oracle")
+    p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--detail", action="store_true", help="per-shape timings on stderr")
+    return p.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def lin_bytes(M, N, K):
+    return 2 * M * K + 4 * K + N * K + 4 * N + 2 * M * N
+
+
+def gemm_bytes(M, N, K):
+    return M * K + 4 * M + N * K + 4 * N + 2 * M * N
+
+
+class Setup:
+    """Device buffers for all layers and token counts."""
+
+    def __init__(self, torch, W, WL, ms):
+        self.torch, self.W = torch, W
+        wl = WL.WORKLOADS["llama8b_decode"]
+        self.shapes = wl.shapes
+        self.ms = ms
+        dev = "cuda"
+        self.s, self.sw, self.wq = {}, {}, {}
+        self.x, self.y, self.ws, self.xq, self.st = {}, {}, {}, {}, {}
+        t0 = time.time()
+        for proj, N, K in self.shapes:
+            outl = WL.outlier_channels(K, wl.outlier_frac, wl.name)
+            xcal = WL.activations(PREFILL_M, K, wl.name, proj, 0, outliers=outl,
+                                  mult=wl.outlier_mult)
+            w = WL.weights(N, K, wl.w_std, wl.name, proj, 0)
+            xcal_d = self.bf16(xcal)
+            w_d = self.bf16(w)
+            # offline prep on the GPU: calibrate, smooth, quantize per channel
+            s = W.w8a8_smoothing_factors(W.w8a8_channel_absmax(xcal_d), W.w8a8_channel_absmax(w_d))
+            wq, sw = W.w8a8_quantize_weight(w_d, s)
+            del w_d
+            self.s[proj], self.sw[proj] = s, sw
+            # layer 0 owns the prepared weight; layers 1.. get copies in
+            # distinct buffers so every layer streams its own bytes from HBM
+            self.wq[proj] = [wq] + [wq.clone() for _ in range(LAYERS - 1)]
+            for M in ms:
+                xm = xcal_d[:M].clone() if M == PREFILL_M else self.bf16(
+                    WL.activations(M, K, wl.name, proj, 0, outliers=outl, mult=wl.outlier_mult))
+                self.x[proj, M] = xm
+                self.y[proj, M] = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+                nb = W.w8a8_linear_workspace_bytes(M, K)
+                self.ws[proj, M] = torch.empty((nb,), dtype=torch.uint8, device=dev)
+                off = (M * K + 255) // 256 * 256
+                self.xq[proj, M] = self.ws[proj, M][:M * K].view(torch.int8).view(M, K)
+                self.st[proj, M] = self.ws[proj, M][off:off + 4 * M].view(torch.float32)
+            del xcal_d
+        torch.cuda.synchronize()
+        log(f"[bench] setup {time.time() - t0:.1f}s, "
+            f"{torch.cuda.memory_allocated() / 2**30:.1f} GiB on device")
+
+    def bf16(self, u16):
+        import numpy as np
+        t = self.torch.from_numpy(np.ascontiguousarray(u16).view(np.int16))
+        return t.cuda().view(self.torch.bfloat16)
+
+    def linear(self, proj, M, layer):
+        W = self.W
+        W.w8a8_linear(self.x[proj, M], self.s[proj], self.wq[proj][layer], self.sw[proj],
+                      y=self.y[proj, M], workspace=self.ws[proj, M])
+
+    def quantize(self, proj, M):
+        self.W.w8a8_quantize_act(self.x[proj, M], self.s[proj], xq=self.xq[proj, M],
+                                 s_tok=self.st[proj, M])
+
+    def gemm(self, proj, M, layer):
+        self.W.w8a8_gemm(self.xq[proj, M], self.st[proj, M], self.wq[proj][layer],
+                         self.sw[proj], y=self.y[proj, M])
+
+
+def capture(torch, fn):
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(torch, g, steps, warmup):
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps          # ms per replay
+
+
+def run_phase(torch, S, ms, steps, warmup, detail):
+    """Times one step (all layers, projections, token counts) and its GEMMs."""
+    def step():
+        for M in ms:
+            for layer in range(LAYERS):
+                for proj, _, _ in S.shapes:
+                    S.linear(proj, M, layer)
+
+    def gemms():
+        for M in ms:
+            for layer in range(LAYERS):
+                for proj, _, _ in S.shapes:
+                    S.gemm(proj, M, layer)
+
+    for M in ms:                     # fill the workspaces the GEMM graph reads
+        for proj, _, _ in S.shapes:
+            S.quantize(proj, M)
+    g_step = capture(torch, step)
+    ms_step = time_graph(torch, g_step, steps, warmup)
+    g_gemm = capture(torch, gemms)
+    ms_gemm = time_graph(torch, g_gemm, steps, warmup)
+    launches = len(ms) * LAYERS * len(S.shapes)
+    per = {}
+    if detail:
+        for M in ms:
+            for proj, N, K in S.shapes:
+                g = capture(torch, lambda: [S.linear(proj, M, l) for l in range(LAYERS)])
+                t = time_graph(torch, g, max(steps // 4, 2), 2) / LAYERS
+                g2 = capture(torch, lambda: [S.gemm(proj, M, l) for l in range(LAYERS)])
+                t2 = time_graph(torch, g2, max(steps // 4, 2), 2) / LAYERS
+                per[f"{proj}_M{M}"] = {"linear_us": round(t * 1e3, 2), "gemm_us": round(t2 * 1e3, 2),
+                                       "linear_GBps": round(lin_bytes(M, N, K) / (t * 1e-3) / 1e9, 1),
+                                       "gemm_GBps": round(gemm_bytes(M, N, K) / (t2 * 1e-3) / 1e9, 1),
+                                       "gemm_TOPS": round(2 * M * N * K / (t2 * 1e-3) / 1e12, 1)}
+                log(f"[bench] {proj:8s} M={M:5d}: linear {t*1e3:8.2f} us  gemm {t2*1e3:8.2f} us  "
+                    f"{per[f'{proj}_M{M}']}")
+    return ms_step, ms_gemm, launches, per
+
+
+def cpu_baseline(W, WL, sample_ms, min_seconds=10.0):
+    """The oracle, timed on this host on one layer of the decode workload."""
+    import numpy as np
+    from oracle import w8a8_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    wl = WL.WORKLOADS["llama8b_decode"]
+    prepared = []
+    for proj, N, K in wl.shapes:
+        outl = WL.outlier_channels(K, wl.outlier_frac, wl.name)
+        xcal = WL.activations(PREFILL_M, K, wl.name, proj, 0, outliers=outl, mult=wl.outlier_mult)
+        w = WL.weights(N, K, wl.w_std, wl.name, proj, 0)
+        aw = np.zeros(K, np.float32)
+        for r0 in range(0, N, 4096):
+            aw = np.maximum(aw, O.weight_channel_absmax(w[r0:r0 + 4096]))
+        s = O.smoothing_factors(O.act_channel_absmax(xcal), aw)
+        parts = [O.prepare_weight(w[r0:r0 + 4096], s) for r0 in range(0, N, 4096)]
+        wq = np.concatenate([p[0] for p in parts])
+        sw = np.concatenate([p[1] for p in parts])
+        xs = {M: WL.activations(M, K, wl.name, proj, 0, outliers=outl, mult=wl.outlier_mult)
+              for M in sample_ms}
+        prepared.append((proj, N, K, s, wq, sw, xs))
+    nbytes, t, passes = 0, 0.0, 0
+    while t < min_seconds:                  # whole passes until the budget is spent
+        for M in sample_ms:
+            for proj, N, K, s, wq, sw, xs in prepared:
+                t0 = time.perf_counter()
+                O.linear(xs[M], s, wq, sw)
+                t += time.perf_counter() - t0
+                nbytes += lin_bytes(M, N, K)
+        passes += 1
+    return {"value": round(nbytes / t / 1e9, 3), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{passes} pass(es) over one layer (qkv, o, gate_up, down) of the decode "
+                      f"workload at M in {list(sample_ms)}: {passes * len(sample_ms) * 4} oracle "
+                      f"linears, {nbytes / 1e9:.2f} GB algorithmic, {t:.1f} s of oracle time; "
+                      f"weight prep untimed"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this layer is measured on one GPU; --gpus {args.gpus} is not "
+              "supported (sharding across GPUs is a design note, not a code path)",
+              file=sys.stderr)
+        sys.exit(2)
+    root = os.path.dirname(os.path.abspath(__file__))
+    sys.path.insert(0, root)
+    import torch
+    import int8_w8a8_quantized_token_amd as W
+    from int8_w8a8_quantized_token_amd import workloads as WL
+    W.lib()                                           # fail loudly if not built
+    torch.cuda.set_device(0)
+
+    ms_all = DECODE_MS + (() if args.no_prefill else (PREFILL_M,))
+    S = Setup(torch, W, WL, ms_all)
+
+    # decode (headline)
+    d_step, d_gemm, d_launch, d_per = run_phase(torch, S, DECODE_MS, args.steps, args.warmup,
+                                                args.detail)
+    d_bytes = sum(lin_bytes(M, N, K) for M in DECODE_MS for _, N, K in S.shapes) * LAYERS
+    d_gbytes = sum(gemm_bytes(M, N, K) for M in DECODE_MS for _, N, K in S.shapes) * LAYERS
+    value = d_bytes / (d_step * 1e-3) / 1e9
+    gemm_gbps = d_gbytes / (d_gemm * 1e-3) / 1e9
+    log(f"[bench] decode step {d_step:.3f} ms -> {value:.0f} GB/s; GEMMs alone "
+        f"{d_gemm:.3f} ms ({d_gemm / d_launch * 1e3:.2f} us/launch) -> {gemm_gbps:.0f} GB/s")
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(d_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "i8",
+        "data": "synthetic",
+        "config": {"workload": "llama8b_decode: Llama-3.1-8B qkv/o/gate_up/down, 32 layers, "
+                               "M in {1,4,16,64}, w8a8_linear per projection",
+                   "layers": LAYERS, "ms": list(DECODE_MS),
+                   "shapes_NK": {p: [n, k] for p, n, k in S.shapes}},
+        "roofline": {"bound": "hbm", "achieved": round(gemm_gbps, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gemm_gbps / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "gemm_skinny_kernel", "launches_per_step": d_launch,
+                     "avg_launch_us": round(d_gemm / d_launch * 1e3, 3)},
+    }
+    if d_per:
+        out["per_shape_decode"] = d_per
+
+    if not args.no_prefill:
+        p_step, p_gemm, p_launch, p_per = run_phase(torch, S, (PREFILL_M,), max(args.steps // 4, 3),
+                                                    min(args.warmup, 2), args.detail)
+        ops = sum(2 * PREFILL_M * N * K for _, N, K in S.shapes) * LAYERS
+        tops = ops / (p_step * 1e-3) / 1e12
+        gtops = ops / (p_gemm * 1e-3) / 1e12
+        log(f"[bench] prefill step {p_step:.3f} ms -> {tops:.0f} TOPS; GEMMs alone "
+            f"{p_gemm:.3f} ms -> {gtops:.0f} TOPS")
+        out["prefill"] = {
+            "value": round(tops, 1), "unit": "TOPS", "ms_per_step": round(p_step, 4),
+            "config": {"workload": "llama8b_prefill: same 32 layers x 4 projections at M=4096",
+                       "m": PREFILL_M},
+            "roofline": {"bound": "mfma", "achieved": round(gtops, 1), "peak": INT8_PEAK_TOPS,
+                         "unit": "TOPS", "frac": round(gtops / INT8_PEAK_TOPS, 4),
+                         "traffic": None, "kernel": "gemm_tiled_kernel",
+                         "launches_per_step": p_launch,
+                         "avg_launch_us": round(p_gemm / p_launch * 1e3, 3)},
+        }
+        if p_per:
+            out["per_shape_prefill"] = p_per
+
+    if not args.no_cpu_baseline:
+        t0 = time.time()
+        out["cpu_baseline"] = cpu_baseline(W, WL, DECODE_MS)
+        log(f"[bench] cpu baseline {time.time() - t0:.1f}s: {out['cpu_baseline']}")
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,188 @@
+/*
+ * w8a8.h -- C ABI of the MI355X (gfx950) W8A8 INT8 linear layer.
+ *
+ * The layer is the one the Red Hat articles "Understanding W8A8 INT8 LLM
+ * quantization: Half the size, better performance, same accuracy" (part 1)
+ * and "... Accuracy and performance results" (part 2) describe: activations
+ * are quantized per token at run time, multiplied as int8 against int8
+ * weights that carry one scale per output channel, and the int32 result is
+ * converted back to bf16.
+ *
+ * Conventions for every entry point below
+ *   - Data pointers are DEVICE pointers on the current HIP device unless a
+ *     parameter says otherwise. bf16 tensors are passed as raw 16-bit words
+ *     (uint16_t). Scales and smoothing factors are IEEE binary32.
+ *   - Matrices are row-major with the last dimension contiguous; ld* is the
+ *     distance between consecutive rows, in elements.
+ *       X, Xq : [M, K]   tokens x input channels
+ *       W, Wq : [N, K]   output channels x input channels
+ *       Y, acc: [M, N]
+ *   - Every call is enqueued on `stream` (0 = the null stream) and returns
+ *     before the GPU work completes. The caller owns all memory; inputs and
+ *     outputs must stay valid until the stream reaches the call. The library
+ *     never allocates device memory and keeps no state between calls.
+ *   - Arguments are validated on the host before any HIP call. A failed
+ *     check returns an error status and enqueues nothing. Device faults
+ *     surface at the caller's next synchronization, as for any HIP kernel.
+ *   - No C++ exception crosses this interface.
+ *   - M == 0 or N == 0 is a valid empty call: W8A8_SUCCESS, nothing launched.
+ *   - Requirements shared by the entry points that read int8/bf16 rows:
+ *       K % 16 == 0, 0 < K <= 131072 (so |acc| <= 128*128*K stays in int32);
+ *       pointers to K-long rows (x, xq, w, wq) 16-byte aligned, with
+ *       ld * element_size a multiple of 16. Outputs with N columns (y, acc)
+ *       need only element alignment and any ld >= N.
+ *     Violations give W8A8_ERROR_UNSUPPORTED (K) or W8A8_ERROR_MISALIGNED.
+ *   - Thread-safe: calls on different streams may run concurrently.
+ */
+#ifndef W8A8_H
+#define W8A8_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define W8A8_ABI_VERSION 1
+
+typedef enum {
+  W8A8_SUCCESS = 0,
+  W8A8_ERROR_INVALID_VALUE = 1, /* NULL required pointer, negative size, ld too small */
+  W8A8_ERROR_MISALIGNED = 2,    /* pointer or row stride below required alignment   */
+  W8A8_ERROR_UNSUPPORTED = 3,   /* K % 16 != 0, K > 131072, size overflow           */
+  W8A8_ERROR_WORKSPACE = 4,     /* workspace NULL or smaller than required          */
+  W8A8_ERROR_HIP = 5            /* the HIP runtime rejected a kernel launch         */
+} w8a8_status_t;
+
+/* Static, NUL-terminated description of a status code. Never NULL. */
+const char* w8a8_status_string(w8a8_status_t status);
+
+/* W8A8_ABI_VERSION of the loaded library. */
+int w8a8_abi_version(void);
+
+/*
+ * Per-token dynamic activation quantization (smooth, scale, round, clamp).
+ *   x'[m,k]  = x[m,k] / smooth[k]                (binary32 division; skipped
+ *                                                  when smooth == NULL)
+ *   s_tok[m] = max_k |x'[m,k]| / 127              (binary32)
+ *   xq[m,k]  = clamp(round(x'[m,k] / s_tok[m]), -127, 127), round half away
+ *              from zero; a row whose absmax is 0 gets s_tok = 0, xq = 0.
+ * Cited: part 1, "Why activation quantization is hard, and how SmoothQuant
+ * fixes it" (one scale per token across its channels, computed at run time)
+ * and "How SmoothQuant prevents outliers in activation tensors" (the
+ * smoothing division and the rounding of the worked example); part 2,
+ * "Inter-token latency (ITL)" (measure range, compute scale, convert).
+ *   x      [M, K] bf16, row stride ldx >= K          (read)
+ *   smooth [K] fp32, every entry finite and > 0, or NULL (read)
+ *   xq     [M, K] int8, row stride ldq >= K          (written)
+ *   s_tok  [M] fp32                                  (written)
+ */
+w8a8_status_t w8a8_quantize_act(const uint16_t* x, int64_t ldx, const float* smooth,
+                                int64_t M, int64_t K, int8_t* xq, int64_t ldq,
+                                float* s_tok, hipStream_t stream);
+
+/*
+ * Int8 GEMM with the dequantizing epilogue.
+ *   acc[m,n] = sum_k xq[m,k] * wq[n,k]              (exact int32)
+ *   y[m,n]   = bf16_rne((float(acc) * s_tok[m]) * s_chan[n])
+ * Cited: part 1, "How we compressed the model" (int8 x int8 matrix multiply
+ * on int8 matrix units) and "Why activation quantization is hard" (the
+ * per-token scale factors out of the channel sum and is applied after it);
+ * part 2, "Inter-token latency (ITL)" (convert back to bf16).
+ * M <= 64 takes the skinny decode kernel, larger M the tiled MFMA kernel;
+ * both give identical results.
+ *   xq [M, K] int8, ldq >= K;  s_tok [M] fp32          (read)
+ *   wq [N, K] int8, ldw >= K;  s_chan [N] fp32         (read)
+ *   y  [M, N] bf16, ldy >= N                           (written)
+ */
+w8a8_status_t w8a8_gemm(const int8_t* xq, int64_t ldq, const float* s_tok,
+                        const int8_t* wq, int64_t ldw, const float* s_chan,
+                        int64_t M, int64_t N, int64_t K,
+                        uint16_t* y, int64_t ldy, hipStream_t stream);
+
+/*
+ * The same GEMM kernels with an int32 epilogue: acc[m,n] = sum_k xq*wq.
+ * Exposes the accumulators for bit-exact checks. ldc >= N, acc 4-byte
+ * aligned.
+ */
+w8a8_status_t w8a8_gemm_i32(const int8_t* xq, int64_t ldq,
+                            const int8_t* wq, int64_t ldw,
+                            int64_t M, int64_t N, int64_t K,
+                            int32_t* acc, int64_t ldc, hipStream_t stream);
+
+/*
+ * Bytes of workspace w8a8_linear needs for M tokens and K input channels:
+ * xq [M, K] int8 followed by s_tok [M] fp32, each 256-byte aligned.
+ * Returns 0 for M <= 0 or K <= 0.
+ */
+size_t w8a8_linear_workspace_bytes(int64_t M, int64_t K);
+
+/*
+ * The whole linear: w8a8_quantize_act into the workspace, then w8a8_gemm,
+ * in stream order. One quantize-dequantize cycle per call, as part 2,
+ * "Inter-token latency (ITL)" counts them per layer and request.
+ *   x [M, K] bf16, ldx >= K; smooth [K] or NULL         (read)
+ *   wq [N, K] int8, ldw >= K; s_chan [N]                (read)
+ *   y [M, N] bf16, ldy >= N                             (written)
+ *   workspace: device memory of at least
+ *              w8a8_linear_workspace_bytes(M, K) bytes, 256-byte aligned;
+ *              overwritten; must not be shared by calls that may overlap.
+ */
+w8a8_status_t w8a8_linear(const uint16_t* x, int64_t ldx, const float* smooth,
+                          const int8_t* wq, int64_t ldw, const float* s_chan,
+                          int64_t M, int64_t N, int64_t K,
+                          uint16_t* y, int64_t ldy,
+                          void* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+
+/* ----------------------------------------------------------------------- *
+ * Offline preparation (calibration and weight quantization). These run
+ * once per model, not per token, but use the same arithmetic on the GPU.
+ * ----------------------------------------------------------------------- */
+
+/*
+ * Per-channel absolute maximum over rows, accumulated:
+ *   absmax[k] = max(absmax[k], max_r |a[r,k]|)
+ * Used on calibration activations (rows = tokens; call once per batch) and
+ * on weights (rows = output channels: the page's "row j of the receiving
+ * layer's weight" in its K x N layout). Cited: part 1, "How the SmoothQuant
+ * smoothing factor is computed".
+ *   a [rows, K] bf16, lda >= K (read);  absmax [K] fp32, >= 0 (read+written;
+ *   zero it before the first batch). K % 8 == 0 suffices here.
+ */
+w8a8_status_t w8a8_channel_absmax(const uint16_t* a, int64_t lda, int64_t rows,
+                                  int64_t K, float* absmax, hipStream_t stream);
+
+/*
+ * SmoothQuant factors with migration strength 1/2:
+ *   smooth[k] = sqrt(act_absmax[k] / w_absmax[k])   (binary32 division and
+ *               square root, correctly rounded); 1 where either input is 0.
+ * Cited: part 1, "How the SmoothQuant smoothing factor is computed" (terms
+ * of the factor; the article's own run uses strength 0.8).
+ *   act_absmax, w_absmax [K] fp32 (read); smooth [K] fp32 (written). Any K >= 0.
+ */
+w8a8_status_t w8a8_smoothing_factors(const float* act_absmax, const float* w_absmax,
+                                     int64_t K, float* smooth, hipStream_t stream);
+
+/*
+ * Smooth and quantize a weight per output channel (symmetric round to nearest):
+ *   w'[n,k]   = bf16_rne(float(w[n,k]) * smooth[k])    (smooth == NULL: w' = w)
+ *   s_chan[n] = max_k |w'[n,k]| / 127
+ *   wq[n,k]   = clamp(round(w'[n,k] / s_chan[n]), -127, 127), half away from 0
+ * Cited: part 1, "The problem with naive quantization" (one scale per weight
+ * channel) and "How the SmoothQuant smoothing factor is computed" (weights
+ * scaled up by the factor, still bf16, before quantization).
+ *   w [N, K] bf16, ldw >= K; smooth [K] or NULL (read)
+ *   wq [N, K] int8, ldwq >= K; s_chan [N] fp32  (written)
+ */
+w8a8_status_t w8a8_quantize_weight(const uint16_t* w, int64_t ldw, const float* smooth,
+                                   int64_t N, int64_t K, int8_t* wq, int64_t ldwq,
+                                   float* s_chan, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W8A8_H */

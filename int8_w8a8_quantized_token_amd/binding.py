@@ -1,0 +1,237 @@
+"""ctypes binding of libw8a8.so: one Python function per C entry point, same
+names, argument marshalling only.
+
+torch is used for device memory (outputs and workspaces are allocated with
+torch.empty when the caller does not pass them) and for the current HIP
+stream. Every step of the layer runs in the library's kernels. If the
+library is missing the first call raises; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libw8a8.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "w8a8.h")
+
+STATUS = {0: "W8A8_SUCCESS", 1: "W8A8_ERROR_INVALID_VALUE", 2: "W8A8_ERROR_MISALIGNED",
+          3: "W8A8_ERROR_UNSUPPORTED", 4: "W8A8_ERROR_WORKSPACE", 5: "W8A8_ERROR_HIP"}
+
+
+class W8A8Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} "
+                         f"({lib().w8a8_status_string(status).decode()})")
+
+
+_p, _i64, _sz, _i = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
+
+_SIGNATURES = {
+    "w8a8_status_string": (ctypes.c_char_p, [_i]),
+    "w8a8_abi_version": (_i, []),
+    "w8a8_quantize_act": (_i, [_p, _i64, _p, _i64, _i64, _p, _i64, _p, _p]),
+    "w8a8_gemm": (_i, [_p, _i64, _p, _p, _i64, _p, _i64, _i64, _i64, _p, _i64, _p]),
+    "w8a8_gemm_i32": (_i, [_p, _i64, _p, _i64, _i64, _i64, _i64, _p, _i64, _p]),
+    "w8a8_linear_workspace_bytes": (_sz, [_i64, _i64]),
+    "w8a8_linear": (_i, [_p, _i64, _p, _p, _i64, _p, _i64, _i64, _i64, _p, _i64, _p, _sz, _p]),
+    "w8a8_channel_absmax": (_i, [_p, _i64, _i64, _i64, _p, _p]),
+    "w8a8_smoothing_factors": (_i, [_p, _p, _i64, _p, _p]),
+    "w8a8_quantize_weight": (_i, [_p, _i64, _p, _i64, _i64, _p, _i64, _p, _p]),
+}
+
+_LIB = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it has not been built)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m int8_w8a8_quantized_token_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype, fn.argtypes = res, args
+        _LIB = handle
+    return _LIB
+
+
+def header_functions() -> list:
+    """Names of the functions include/w8a8.h declares."""
+    with open(HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(w8a8_[a-z0-9_]+)\s*\(", text)))
+
+
+# ---------------------------------------------------------------------------
+# torch-facing marshalling
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _mat(t, dtypes, name):
+    torch = _torch()
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name}: need a 2-D tensor with a contiguous last dim")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: must be a device tensor")
+    return t.data_ptr(), (t.stride(0) if t.shape[0] > 1 else max(t.shape[1], t.stride(0)))
+
+
+def _vec(t, name, dtype=None):
+    if t is None:
+        return None
+    torch = _torch()
+    dtype = dtype or torch.float32
+    if t.dtype != dtype or t.dim() != 1 or (t.numel() > 1 and t.stride(0) != 1):
+        raise TypeError(f"{name}: need a contiguous 1-D {dtype} tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: must be a device tensor")
+    return t.data_ptr()
+
+
+def _check(status, where):
+    if status != 0:
+        raise W8A8Error(status, where)
+
+
+def _bf16_types():
+    torch = _torch()
+    return (torch.bfloat16, torch.int16)
+
+
+def w8a8_status_string(status: int) -> str:
+    return lib().w8a8_status_string(status).decode()
+
+
+def w8a8_abi_version() -> int:
+    return lib().w8a8_abi_version()
+
+
+def w8a8_quantize_act(x, smooth=None, xq=None, s_tok=None, stream=None):
+    """x bf16 [M, K] -> (xq int8 [M, K], s_tok fp32 [M])."""
+    torch = _torch()
+    M, K = x.shape
+    if xq is None:
+        xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    if s_tok is None:
+        s_tok = torch.empty((M,), dtype=torch.float32, device=x.device)
+    px, ldx = _mat(x, _bf16_types(), "x")
+    pq, ldq = _mat(xq, (torch.int8,), "xq")
+    _check(lib().w8a8_quantize_act(px, ldx, _vec(smooth, "smooth"), M, K, pq, ldq,
+                                   _vec(s_tok, "s_tok"), _stream(stream)), "w8a8_quantize_act")
+    return xq, s_tok
+
+
+def w8a8_gemm(xq, s_tok, wq, s_chan, y=None, stream=None):
+    """(xq [M, K], s_tok [M]) x (wq [N, K], s_chan [N]) -> y bf16 [M, N]."""
+    torch = _torch()
+    M, K = xq.shape
+    N = wq.shape[0]
+    if wq.shape[1] != K:
+        raise ValueError("xq and wq disagree on K")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
+    pq, ldq = _mat(xq, (torch.int8,), "xq")
+    pw, ldw = _mat(wq, (torch.int8,), "wq")
+    py, ldy = _mat(y, _bf16_types(), "y")
+    _check(lib().w8a8_gemm(pq, ldq, _vec(s_tok, "s_tok"), pw, ldw, _vec(s_chan, "s_chan"),
+                           M, N, K, py, ldy, _stream(stream)), "w8a8_gemm")
+    return y
+
+
+def w8a8_gemm_i32(xq, wq, acc=None, stream=None):
+    """Exact int32 accumulators acc [M, N] = xq @ wq.T."""
+    torch = _torch()
+    M, K = xq.shape
+    N = wq.shape[0]
+    if wq.shape[1] != K:
+        raise ValueError("xq and wq disagree on K")
+    if acc is None:
+        acc = torch.empty((M, N), dtype=torch.int32, device=xq.device)
+    pq, ldq = _mat(xq, (torch.int8,), "xq")
+    pw, ldw = _mat(wq, (torch.int8,), "wq")
+    pc, ldc = _mat(acc, (torch.int32,), "acc")
+    _check(lib().w8a8_gemm_i32(pq, ldq, pw, ldw, M, N, K, pc, ldc, _stream(stream)),
+           "w8a8_gemm_i32")
+    return acc
+
+
+def w8a8_linear_workspace_bytes(M: int, K: int) -> int:
+    return lib().w8a8_linear_workspace_bytes(M, K)
+
+
+def w8a8_linear(x, smooth, wq, s_chan, y=None, workspace=None, stream=None):
+    """x bf16 [M, K] -> y bf16 [M, N] (quantize + GEMM + epilogue)."""
+    torch = _torch()
+    M, K = x.shape
+    N = wq.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    nbytes = w8a8_linear_workspace_bytes(M, K)
+    if workspace is None:
+        workspace = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=x.device)
+    px, ldx = _mat(x, _bf16_types(), "x")
+    pw, ldw = _mat(wq, (torch.int8,), "wq")
+    py, ldy = _mat(y, _bf16_types(), "y")
+    _check(lib().w8a8_linear(px, ldx, _vec(smooth, "smooth"), pw, ldw, _vec(s_chan, "s_chan"),
+                             M, N, K, py, ldy, workspace.data_ptr(),
+                             workspace.numel() * workspace.element_size(), _stream(stream)),
+           "w8a8_linear")
+    return y
+
+
+def w8a8_channel_absmax(a, absmax=None, stream=None):
+    """absmax [K] = max(absmax, max over rows |a|); zero-initialized if not given."""
+    torch = _torch()
+    rows, K = a.shape
+    if absmax is None:
+        absmax = torch.zeros((K,), dtype=torch.float32, device=a.device)
+    pa, lda = _mat(a, _bf16_types(), "a")
+    _check(lib().w8a8_channel_absmax(pa, lda, rows, K, _vec(absmax, "absmax"), _stream(stream)),
+           "w8a8_channel_absmax")
+    return absmax
+
+
+def w8a8_smoothing_factors(act_absmax, w_absmax, smooth=None, stream=None):
+    torch = _torch()
+    K = act_absmax.shape[0]
+    if smooth is None:
+        smooth = torch.empty((K,), dtype=torch.float32, device=act_absmax.device)
+    _check(lib().w8a8_smoothing_factors(_vec(act_absmax, "act_absmax"), _vec(w_absmax, "w_absmax"),
+                                        K, _vec(smooth, "smooth"), _stream(stream)),
+           "w8a8_smoothing_factors")
+    return smooth
+
+
+def w8a8_quantize_weight(w, smooth=None, wq=None, s_chan=None, stream=None):
+    """w bf16 [N, K] -> (wq int8 [N, K], s_chan fp32 [N])."""
+    torch = _torch()
+    N, K = w.shape
+    if wq is None:
+        wq = torch.empty((N, K), dtype=torch.int8, device=w.device)
+    if s_chan is None:
+        s_chan = torch.empty((N,), dtype=torch.float32, device=w.device)
+    pw, ldw = _mat(w, _bf16_types(), "w")
+    pq, ldq = _mat(wq, (torch.int8,), "wq")
+    _check(lib().w8a8_quantize_weight(pw, ldw, _vec(smooth, "smooth"), N, K, pq, ldq,
+                                      _vec(s_chan, "s_chan"), _stream(stream)),
+           "w8a8_quantize_weight")
+    return wq, s_chan

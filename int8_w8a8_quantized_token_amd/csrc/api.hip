@@ -1,0 +1,183 @@
+// C ABI of the W8A8 INT8 linear layer: argument validation (host only, before
+// any HIP call) and dispatch to the gfx950 kernel launchers.
+
+#include <limits.h>
+#include <stdint.h>
+
+#include "../../include/w8a8.h"
+#include "launchers.h"
+
+namespace {
+
+constexpr int64_t kMaxK = 131072;  // 128 * 128 * K stays below 2^31
+constexpr int64_t kMaxDim = INT32_MAX;
+
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+// Checks a row-major [rows, cols] operand with row stride ld (elements).
+w8a8_status_t check_matrix(const void* p, int64_t ld, int64_t rows, int64_t cols, int64_t elem) {
+  if (p == nullptr || ld < cols) return W8A8_ERROR_INVALID_VALUE;
+  if (ld > (INT64_MAX / 4) / elem / (rows > 0 ? rows : 1)) return W8A8_ERROR_UNSUPPORTED;
+  if (!aligned(p, 16) || (ld * elem) % 16 != 0) return W8A8_ERROR_MISALIGNED;
+  return W8A8_SUCCESS;
+}
+
+// Output matrices need only element alignment; the kernels use vector stores
+// when the base and row stride allow them.
+w8a8_status_t check_out_matrix(const void* p, int64_t ld, int64_t rows, int64_t cols,
+                               int64_t elem) {
+  if (p == nullptr || ld < cols) return W8A8_ERROR_INVALID_VALUE;
+  if (ld > (INT64_MAX / 4) / elem / (rows > 0 ? rows : 1)) return W8A8_ERROR_UNSUPPORTED;
+  if (!aligned(p, (uintptr_t)elem)) return W8A8_ERROR_MISALIGNED;
+  return W8A8_SUCCESS;
+}
+
+w8a8_status_t check_vector(const void* p) {
+  if (p == nullptr) return W8A8_ERROR_INVALID_VALUE;
+  if (!aligned(p, 4)) return W8A8_ERROR_MISALIGNED;
+  return W8A8_SUCCESS;
+}
+
+// Size checks common to the row-reading entry points.
+w8a8_status_t check_dims(int64_t rows, int64_t K, int64_t N = 1) {
+  if (rows < 0 || K < 0 || N < 0) return W8A8_ERROR_INVALID_VALUE;
+  if (K == 0) return W8A8_ERROR_INVALID_VALUE;
+  if (K % 16 != 0 || K > kMaxK || rows > kMaxDim || N > kMaxDim) return W8A8_ERROR_UNSUPPORTED;
+  return W8A8_SUCCESS;
+}
+
+w8a8_status_t from_hip(hipError_t e) { return e == hipSuccess ? W8A8_SUCCESS : W8A8_ERROR_HIP; }
+
+#define W8A8_TRY(expr)                      \
+  do {                                      \
+    const w8a8_status_t st_ = (expr);       \
+    if (st_ != W8A8_SUCCESS) return st_;    \
+  } while (0)
+
+w8a8_status_t validate_gemm(const int8_t* xq, int64_t ldq, const int8_t* wq, int64_t ldw,
+                            int64_t M, int64_t N, int64_t K) {
+  W8A8_TRY(check_matrix(xq, ldq, M, K, 1));
+  W8A8_TRY(check_matrix(wq, ldw, N, K, 1));
+  return W8A8_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* w8a8_status_string(w8a8_status_t status) {
+  switch (status) {
+    case W8A8_SUCCESS: return "success";
+    case W8A8_ERROR_INVALID_VALUE: return "invalid value (null pointer, negative size or leading dimension too small)";
+    case W8A8_ERROR_MISALIGNED: return "misaligned pointer or row stride";
+    case W8A8_ERROR_UNSUPPORTED: return "unsupported size (K must be a positive multiple of 16, at most 131072)";
+    case W8A8_ERROR_WORKSPACE: return "workspace missing or too small";
+    case W8A8_ERROR_HIP: return "HIP kernel launch failed";
+  }
+  return "unknown status";
+}
+
+int w8a8_abi_version(void) { return W8A8_ABI_VERSION; }
+
+w8a8_status_t w8a8_quantize_act(const uint16_t* x, int64_t ldx, const float* smooth, int64_t M,
+                                int64_t K, int8_t* xq, int64_t ldq, float* s_tok,
+                                hipStream_t stream) {
+  W8A8_TRY(check_dims(M, K));
+  if (M == 0) return W8A8_SUCCESS;
+  W8A8_TRY(check_matrix(x, ldx, M, K, 2));
+  W8A8_TRY(check_matrix(xq, ldq, M, K, 1));
+  W8A8_TRY(check_vector(s_tok));
+  if (smooth) W8A8_TRY(check_vector(smooth));
+  return from_hip(w8a8::launch_quantize_rows(w8a8::RowMode::kActivation, x, ldx, smooth, M, K, xq,
+                                             ldq, s_tok, stream));
+}
+
+w8a8_status_t w8a8_gemm(const int8_t* xq, int64_t ldq, const float* s_tok, const int8_t* wq,
+                        int64_t ldw, const float* s_chan, int64_t M, int64_t N, int64_t K,
+                        uint16_t* y, int64_t ldy, hipStream_t stream) {
+  W8A8_TRY(check_dims(M, K, N));
+  if (M == 0 || N == 0) return W8A8_SUCCESS;
+  W8A8_TRY(validate_gemm(xq, ldq, wq, ldw, M, N, K));
+  W8A8_TRY(check_vector(s_tok));
+  W8A8_TRY(check_vector(s_chan));
+  W8A8_TRY(check_out_matrix(y, ldy, M, N, 2));
+  return from_hip(w8a8::launch_gemm(xq, ldq, s_tok, wq, ldw, s_chan, M, N, K, y, ldy, nullptr, 0,
+                                    stream));
+}
+
+w8a8_status_t w8a8_gemm_i32(const int8_t* xq, int64_t ldq, const int8_t* wq, int64_t ldw,
+                            int64_t M, int64_t N, int64_t K, int32_t* acc, int64_t ldc,
+                            hipStream_t stream) {
+  W8A8_TRY(check_dims(M, K, N));
+  if (M == 0 || N == 0) return W8A8_SUCCESS;
+  W8A8_TRY(validate_gemm(xq, ldq, wq, ldw, M, N, K));
+  W8A8_TRY(check_out_matrix(acc, ldc, M, N, 4));
+  return from_hip(w8a8::launch_gemm(xq, ldq, nullptr, wq, ldw, nullptr, M, N, K, nullptr, 0, acc,
+                                    ldc, stream));
+}
+
+size_t w8a8_linear_workspace_bytes(int64_t M, int64_t K) {
+  if (M <= 0 || K <= 0 || M > kMaxDim || K > kMaxK) return 0;
+  return align256((size_t)M * (size_t)K) + align256((size_t)M * sizeof(float));
+}
+
+w8a8_status_t w8a8_linear(const uint16_t* x, int64_t ldx, const float* smooth, const int8_t* wq,
+                          int64_t ldw, const float* s_chan, int64_t M, int64_t N, int64_t K,
+                          uint16_t* y, int64_t ldy, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+  W8A8_TRY(check_dims(M, K, N));
+  if (M == 0 || N == 0) return W8A8_SUCCESS;
+  W8A8_TRY(check_matrix(x, ldx, M, K, 2));
+  W8A8_TRY(check_matrix(wq, ldw, N, K, 1));
+  W8A8_TRY(check_vector(s_chan));
+  if (smooth) W8A8_TRY(check_vector(smooth));
+  W8A8_TRY(check_out_matrix(y, ldy, M, N, 2));
+  if (workspace == nullptr || workspace_bytes < w8a8_linear_workspace_bytes(M, K))
+    return W8A8_ERROR_WORKSPACE;
+  if (!aligned(workspace, 256)) return W8A8_ERROR_MISALIGNED;
+
+  int8_t* xq = static_cast<int8_t*>(workspace);
+  float* s_tok = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256((size_t)M * K));
+  W8A8_TRY(from_hip(w8a8::launch_quantize_rows(w8a8::RowMode::kActivation, x, ldx, smooth, M, K,
+                                               xq, K, s_tok, stream)));
+  return from_hip(w8a8::launch_gemm(xq, K, s_tok, wq, ldw, s_chan, M, N, K, y, ldy, nullptr, 0,
+                                    stream));
+}
+
+w8a8_status_t w8a8_channel_absmax(const uint16_t* a, int64_t lda, int64_t rows, int64_t K,
+                                  float* absmax, hipStream_t stream) {
+  if (rows < 0 || K <= 0) return W8A8_ERROR_INVALID_VALUE;
+  if (K % 8 != 0 || K > kMaxDim / 8 || rows > kMaxDim) return W8A8_ERROR_UNSUPPORTED;
+  if (rows == 0) return W8A8_SUCCESS;
+  W8A8_TRY(check_matrix(a, lda, rows, K, 2));
+  W8A8_TRY(check_vector(absmax));
+  return from_hip(w8a8::launch_channel_absmax(a, lda, rows, K, absmax, stream));
+}
+
+w8a8_status_t w8a8_smoothing_factors(const float* act_absmax, const float* w_absmax, int64_t K,
+                                     float* smooth, hipStream_t stream) {
+  if (K < 0) return W8A8_ERROR_INVALID_VALUE;
+  if (K > kMaxDim) return W8A8_ERROR_UNSUPPORTED;
+  if (K == 0) return W8A8_SUCCESS;
+  W8A8_TRY(check_vector(act_absmax));
+  W8A8_TRY(check_vector(w_absmax));
+  W8A8_TRY(check_vector(smooth));
+  return from_hip(w8a8::launch_smoothing_factors(act_absmax, w_absmax, K, smooth, stream));
+}
+
+w8a8_status_t w8a8_quantize_weight(const uint16_t* w, int64_t ldw, const float* smooth, int64_t N,
+                                   int64_t K, int8_t* wq, int64_t ldwq, float* s_chan,
+                                   hipStream_t stream) {
+  W8A8_TRY(check_dims(N, K));
+  if (N == 0) return W8A8_SUCCESS;
+  W8A8_TRY(check_matrix(w, ldw, N, K, 2));
+  W8A8_TRY(check_matrix(wq, ldwq, N, K, 1));
+  W8A8_TRY(check_vector(s_chan));
+  if (smooth) W8A8_TRY(check_vector(smooth));
+  return from_hip(w8a8::launch_quantize_rows(w8a8::RowMode::kWeight, w, ldw, smooth, N, K, wq,
+                                             ldwq, s_chan, stream));
+}
+
+}  // extern "C"

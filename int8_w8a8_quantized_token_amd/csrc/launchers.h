@@ -1,0 +1,32 @@
+// Host-side launchers of the gfx950 kernels. Arguments are already
+// validated by the C-ABI layer (api.hip); each launcher only enqueues.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w8a8 {
+
+// Per-row quantization of bf16 rows: activations (x / smooth) or weights
+// (bf16(w * smooth)). Writes int8 codes and one binary32 scale per row.
+enum class RowMode { kActivation = 0, kWeight = 1 };
+
+hipError_t launch_quantize_rows(RowMode mode, const uint16_t* x, int64_t ldx,
+                                const float* smooth, int64_t rows, int64_t K,
+                                int8_t* q, int64_t ldq, float* scale, hipStream_t s);
+
+hipError_t launch_channel_absmax(const uint16_t* a, int64_t lda, int64_t rows, int64_t K,
+                                 float* absmax, hipStream_t s);
+
+hipError_t launch_smoothing_factors(const float* ax, const float* aw, int64_t K,
+                                    float* smooth, hipStream_t s);
+
+// GEMM with either the bf16 dequantizing epilogue (y != nullptr) or the
+// int32 accumulator epilogue (acc != nullptr).
+hipError_t launch_gemm(const int8_t* xq, int64_t ldq, const float* s_tok,
+                       const int8_t* wq, int64_t ldw, const float* s_chan,
+                       int64_t M, int64_t N, int64_t K,
+                       uint16_t* y, int64_t ldy, int32_t* acc, int64_t ldc,
+                       hipStream_t s);
+
+}  // namespace w8a8

@@ -1,0 +1,129 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/w8a8.h declares, and rejects bad arguments on the host before any
+HIP call. Every call below with fake pointers either fails validation or is
+an empty (M == 0 / N == 0) no-op, so nothing is ever launched, even on a
+machine with a GPU."""
+import ctypes
+import subprocess
+
+import pytest
+
+import int8_w8a8_quantized_token_amd as W
+from int8_w8a8_quantized_token_amd import binding as B
+
+OK, INVALID, MISALIGNED, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3, 4
+A = 0x10000          # a fake, 256-byte aligned "device" address
+MIS = A + 8          # 8-byte aligned only
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return W.lib()
+
+
+def test_exports_every_header_function(lib):
+    names = W.header_functions()
+    assert len(names) == 10
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert set(names) <= exported
+
+
+def test_version_and_status_strings(lib):
+    assert W.w8a8_abi_version() == 1
+    for s in range(6):
+        assert isinstance(W.w8a8_status_string(s), str) and W.w8a8_status_string(s)
+    assert W.w8a8_status_string(99) == "unknown status"
+
+
+def test_workspace_bytes(lib):
+    def al(v):
+        return (v + 255) // 256 * 256
+    for M, K in [(1, 16), (16, 4096), (3000, 14336), (7, 48)]:
+        assert W.w8a8_linear_workspace_bytes(M, K) == al(M * K) + al(4 * M)
+    assert W.w8a8_linear_workspace_bytes(0, 4096) == 0
+    assert W.w8a8_linear_workspace_bytes(16, 0) == 0
+
+
+def q(lib, x=A, ldx=4096, smooth=None, M=16, K=4096, xq=A, ldq=4096, s=A):
+    return lib.w8a8_quantize_act(x, ldx, smooth, M, K, xq, ldq, s, None)
+
+
+def test_quantize_act_validation(lib):
+    assert q(lib, x=None) == INVALID
+    assert q(lib, M=-1) == INVALID
+    assert q(lib, K=0) == INVALID
+    assert q(lib, K=24, ldx=24, ldq=24) == UNSUPPORTED
+    assert q(lib, K=131072 + 16, ldx=131088, ldq=131088) == UNSUPPORTED
+    assert q(lib, M=0, x=None, xq=None, s=None) == OK            # empty call, nothing launched
+    assert q(lib, x=MIS) == MISALIGNED
+    assert q(lib, ldx=4100) == MISALIGNED                         # 8200-byte rows
+    assert q(lib, ldx=4000) == INVALID                            # ld < K
+    assert q(lib, ldq=4104) == MISALIGNED
+    assert q(lib, s=None) == INVALID
+    assert q(lib, smooth=A + 2) == MISALIGNED
+
+
+def g(lib, xq=A, ldq=4096, st=A, wq=A, ldw=4096, sc=A, M=16, N=4096, K=4096, y=A, ldy=4096):
+    return lib.w8a8_gemm(xq, ldq, st, wq, ldw, sc, M, N, K, y, ldy, None)
+
+
+def test_gemm_validation(lib):
+    assert g(lib, N=0, xq=None, wq=None, y=None) == OK
+    assert g(lib, M=0, xq=None, wq=None, y=None) == OK
+    assert g(lib, N=-5) == INVALID
+    assert g(lib, y=None) == INVALID
+    assert g(lib, wq=None) == INVALID
+    assert g(lib, sc=None) == INVALID
+    assert g(lib, y=A + 1) == MISALIGNED                         # bf16 needs 2-byte alignment
+    assert g(lib, wq=MIS) == MISALIGNED
+    assert g(lib, K=40, ldq=40, ldw=40) == UNSUPPORTED
+    assert g(lib, ldw=4000) == INVALID
+
+
+def test_gemm_i32_validation(lib):
+    f = lib.w8a8_gemm_i32
+    assert f(A, 64, A, 64, 4, 8, 64, None, 8, None) == INVALID
+    assert f(A, 64, A, 64, 4, 8, 64, A, 6, None) == INVALID     # ldc < N
+    assert f(A, 64, A, 64, 4, 10, 64, A + 2, 10, None) == MISALIGNED  # int32 needs 4 bytes
+    assert f(A, 64, A, 64, 0, 10, 64, None, 10, None) == OK
+
+
+def lin(lib, ws=A, wsb=None, M=16, N=4096, K=4096, x=A):
+    if wsb is None:
+        wsb = W.w8a8_linear_workspace_bytes(M, K)
+    return lib.w8a8_linear(x, K, None, A, K, A, M, N, K, A, N, ws, wsb, None)
+
+
+def test_linear_validation(lib):
+    assert lin(lib, ws=None) == WORKSPACE
+    assert lin(lib, wsb=W.w8a8_linear_workspace_bytes(16, 4096) - 1) == WORKSPACE
+    assert lin(lib, ws=A + 16) == MISALIGNED
+    assert lin(lib, x=None) == INVALID
+    assert lin(lib, M=0, ws=None, x=None) == OK
+    assert lin(lib, K=4104) == UNSUPPORTED
+
+
+def test_prep_validation(lib):
+    ca = lib.w8a8_channel_absmax
+    assert ca(A, 4096, 16, 4096, None, None) == INVALID
+    assert ca(A, 12, 16, 12, A, None) == UNSUPPORTED           # K % 8
+    assert ca(A, 4096, 0, 4096, None, None) == OK
+    assert ca(MIS, 4096, 16, 4096, A, None) == MISALIGNED
+    sf = lib.w8a8_smoothing_factors
+    assert sf(A, A, -1, A, None) == INVALID
+    assert sf(None, None, 0, None, None) == OK
+    assert sf(A, None, 16, A, None) == INVALID
+    qw = lib.w8a8_quantize_weight
+    assert qw(A, 4096, None, 16, 4096, A, 4096, None, None) == INVALID
+    assert qw(A, 4096, None, 16, 4104, A, 4104, A, None) == UNSUPPORTED
+    assert qw(A, 4096, None, 0, 4096, None, 4096, None, None) == OK
+
+
+def test_python_binding_raises_typed_error(lib):
+    torch = pytest.importorskip("torch")
+    with pytest.raises((TypeError, ValueError)):
+        W.w8a8_quantize_act(torch.zeros((4, 16), dtype=torch.float32))

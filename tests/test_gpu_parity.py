@@ -1,0 +1,268 @@
+"""GPU parity of every C-ABI entry point against the CPU oracle, on seeded
+inputs at sizes the oracle finishes in seconds: several tiles of each kernel
+plus ragged M, N and K tails, crafted edge rows (exact ties, zero rows,
+subnormal rows, extremes), strided views and empty calls.
+
+int8 codes, scales and int32 accumulators must be bit-exact; bf16 outputs
+within 1 bf16 ulp (relative error <= 2**-8) of the oracle.
+"""
+import numpy as np
+import pytest
+
+import int8_w8a8_quantized_token_amd as W
+from int8_w8a8_quantized_token_amd import workloads as WL
+from oracle import w8a8_oracle as O
+from gpu_util import check_bf16, dev, dev_bf16, host, torch
+
+pytestmark = pytest.mark.gpu
+
+F32 = np.float32
+
+
+def act(M, K, tag, frac=0.01, mult=20.0):
+    return WL.activations(M, K, "parity", tag, frac=frac, mult=mult)
+
+
+def smooth_for(x_bf16, w_bf16):
+    return O.smoothing_factors(O.act_channel_absmax(x_bf16), O.weight_channel_absmax(w_bf16))
+
+
+def i8(shape, *key):
+    return WL.rng("i8", *shape, *key).integers(-128, 128, size=shape, dtype=np.int64).astype(np.int8)
+
+
+# ---------------------------------------------------------------------------
+# quantize_act
+# ---------------------------------------------------------------------------
+
+QA_SHAPES = [(1, 16), (2, 48), (3, 64), (15, 4096 + 16), (16, 4096), (17, 2048),
+             (63, 512), (64, 14336), (65, 4096), (127, 1040), (255, 256), (4, 40960)]
+
+
+@pytest.mark.parametrize("M,K", QA_SHAPES, ids=[f"M{m}_K{k}" for m, k in QA_SHAPES])
+@pytest.mark.parametrize("use_smooth", [False, True], ids=["plain", "smooth"])
+def test_quantize_act_bit_exact(M, K, use_smooth):
+    x = act(M, K, "qa")
+    smooth = None
+    if use_smooth:
+        smooth = np.exp(WL.rng("smooth", K).uniform(-3, 3, K)).astype(F32)
+    xq_ref, s_ref = O.quantize_act(x, smooth)
+    xq, s = W.w8a8_quantize_act(dev_bf16(x), dev(smooth) if smooth is not None else None)
+    torch().cuda.synchronize()
+    np.testing.assert_array_equal(host(s).view(np.uint32), s_ref.view(np.uint32))
+    np.testing.assert_array_equal(host(xq), xq_ref)
+
+
+def crafted_rows(K):
+    """Rows that exercise ties, zeros, subnormals and extremes (K >= 16).
+    Every value is exactly representable in bf16."""
+    rows = []
+    base = np.zeros(K, F32)
+    # exact ties: row max 127 * 2**k gives S = 2**k, (n + 1/2) * 2**k are ties
+    for k in (-20, -3, 0, 5):
+        r = base.copy()
+        vals = np.array([127, 62.5, -62.5, 0.5, -0.5, 1.5, -1.5, 126.5, -126.5, 2.5, -2.5,
+                         0.25, 63.5, -63.5, 100.5, -0.75], F32)
+        r[:16] = vals * F32(2.0 ** k)
+        rows.append(r)
+    rows.append(base.copy())                                   # all-zero row
+    r = base.copy(); r[3] = F32(-2.0 ** -130); rows.append(r)  # one subnormal value
+    r = np.full(K, F32(2.0 ** -125)); r[::7] = F32(-1.5 * 2.0 ** -125); rows.append(r)
+    r = np.full(K, F32(2.0 ** 100)); r[1] = F32(-1.5 * 2.0 ** 127); rows.append(r)
+    rows.append(O.bf16_to_f32(O.round_to_bf16(np.linspace(-1, 1, K))))   # ramp
+    return np.stack(rows).astype(F32)
+
+
+@pytest.mark.parametrize("K", [16, 64, 4096])
+def test_quantize_act_crafted_rows(K):
+    x32 = crafted_rows(K)
+    x = O.round_to_bf16(x32)
+    assert np.array_equal(O.bf16_to_f32(x), x32), "crafted values must be bf16-exact"
+    xq_ref, s_ref = O.quantize_act(x)
+    xq, s = W.w8a8_quantize_act(dev_bf16(x))
+    torch().cuda.synchronize()
+    np.testing.assert_array_equal(host(s).view(np.uint32), s_ref.view(np.uint32))
+    np.testing.assert_array_equal(host(xq), xq_ref)
+    # the tie rows really hit the tie rule
+    assert host(xq)[2, :16].tolist()[:11] == [127, 63, -63, 1, -1, 2, -2, 127, -127, 3, -3]
+
+
+def test_quantize_act_strided_and_empty():
+    M, K, ld = 33, 4096, 6144
+    big = act(M, ld, "strided")
+    x = dev_bf16(big)[:, :K]                   # a column slice: ldx = 6144
+    xq_full = torch().zeros((M, K + 64), dtype=torch().int8, device="cuda")
+    xq = xq_full[:, :K]
+    _, s = W.w8a8_quantize_act(x, None, xq=xq)
+    torch().cuda.synchronize()
+    xq_ref, s_ref = O.quantize_act(big[:, :K])
+    np.testing.assert_array_equal(host(xq), xq_ref)
+    np.testing.assert_array_equal(host(s), s_ref)
+    assert np.all(host(xq_full)[:, K:] == 0), "wrote past the row"
+    e = torch().empty((0, K), dtype=torch().bfloat16, device="cuda")
+    W.w8a8_quantize_act(e)
+    torch().cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# GEMM: int32 accumulators (bit-exact) and bf16 epilogue (<= 1 ulp)
+# ---------------------------------------------------------------------------
+
+GEMM_SHAPES = [
+    # skinny path (M <= 64)
+    (1, 1, 16), (1, 16, 64), (4, 17, 48), (16, 100, 80), (17, 256, 192), (33, 300, 1040),
+    (48, 64, 4096), (64, 4096, 4096), (5, 6144, 14336 + 16),
+    # tiled path
+    (65, 1, 16), (65, 128, 64), (100, 129, 112), (128, 256, 4096), (130, 300, 1040),
+    (257, 515, 208), (512, 512, 2048), (1000, 384, 4096 + 48),
+]
+
+
+@pytest.mark.parametrize("M,N,K", GEMM_SHAPES, ids=[f"M{m}_N{n}_K{k}" for m, n, k in GEMM_SHAPES])
+def test_gemm_i32_bit_exact(M, N, K):
+    a, b = i8((M, K), "a"), i8((N, K), "b")
+    acc = W.w8a8_gemm_i32(dev(a), dev(b))
+    torch().cuda.synchronize()
+    np.testing.assert_array_equal(host(acc), O.gemm_i32(a, b))
+
+
+def test_gemm_i32_closed_form_extremes():
+    # |acc| at its largest: all 127 x all -127 over K = 28672, both paths
+    K = 28672
+    for M in (16, 96):
+        a = np.full((M, K), 127, np.int8)
+        b = np.full((40, K), -127, np.int8)
+        b[::2] = 127
+        acc = host(W.w8a8_gemm_i32(dev(a), dev(b)))
+        torch().cuda.synchronize()
+        want = np.where(np.arange(40) % 2 == 0, 16129 * K, -16129 * K)
+        assert np.all(acc == want[None, :])
+
+
+@pytest.mark.parametrize("M,N,K", GEMM_SHAPES, ids=[f"M{m}_N{n}_K{k}" for m, n, k in GEMM_SHAPES])
+def test_gemm_bf16_epilogue(M, N, K):
+    a, b = i8((M, K), "a"), i8((N, K), "b")
+    r = WL.rng("scales", M, N, K)
+    s_tok = np.exp(r.uniform(-12, -2, M)).astype(F32)
+    s_chan = np.exp(r.uniform(-10, -3, N)).astype(F32)
+    s_tok[0] = 0.0                              # a zero token scale
+    y = W.w8a8_gemm(dev(a), dev(s_tok), dev(b), dev(s_chan))
+    torch().cuda.synchronize()
+    y64, y_ref = O.dequant_epilogue(O.gemm_i32(a, b), s_tok, s_chan)
+    check_bf16(host(y), y64, y_ref)
+
+
+def test_gemm_strided_output():
+    M, N, K, ldy = 40, 200, 256, 264
+    a, b = i8((M, K), "sa"), i8((N, K), "sb")
+    s_tok = np.full(M, 1e-3, F32)
+    s_chan = np.full(N, 2e-3, F32)
+    yfull = torch().zeros((M, ldy), dtype=torch().bfloat16, device="cuda")
+    W.w8a8_gemm(dev(a), dev(s_tok), dev(b), dev(s_chan), y=yfull[:, :N])
+    torch().cuda.synchronize()
+    y64, y_ref = O.dequant_epilogue(O.gemm_i32(a, b), s_tok, s_chan)
+    yh = host(yfull)
+    check_bf16(yh[:, :N], y64, y_ref)
+    assert np.all(yh[:, N:] == 0), "wrote past the row"
+
+
+# ---------------------------------------------------------------------------
+# offline prep kernels (bit-exact)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("N,K", [(3, 16), (100, 4096), (4096, 4096), (17, 14336)])
+def test_prep_bit_exact(N, K):
+    M = 37
+    x = act(M, K, "prep")
+    w = WL.weights(N, K, 0.02, "prep")
+    ax = W.w8a8_channel_absmax(dev_bf16(x[:20]))
+    W.w8a8_channel_absmax(dev_bf16(x[20:]), absmax=ax)       # accumulate a second batch
+    aw = W.w8a8_channel_absmax(dev_bf16(w))
+    s = W.w8a8_smoothing_factors(ax, aw)
+    wq, sw = W.w8a8_quantize_weight(dev_bf16(w), s)
+    wq0, sw0 = W.w8a8_quantize_weight(dev_bf16(w))
+    torch().cuda.synchronize()
+    ax_ref, aw_ref = O.act_channel_absmax(x), O.weight_channel_absmax(w)
+    np.testing.assert_array_equal(host(ax), ax_ref)
+    np.testing.assert_array_equal(host(aw), aw_ref)
+    s_ref = O.smoothing_factors(ax_ref, aw_ref)
+    np.testing.assert_array_equal(host(s).view(np.uint32), s_ref.view(np.uint32))
+    wq_ref, sw_ref = O.prepare_weight(w, s_ref)
+    np.testing.assert_array_equal(host(sw).view(np.uint32), sw_ref.view(np.uint32))
+    np.testing.assert_array_equal(host(wq), wq_ref)
+    wq0_ref, sw0_ref = O.quantize_weight(w)
+    np.testing.assert_array_equal(host(sw0), sw0_ref)
+    np.testing.assert_array_equal(host(wq0), wq0_ref)
+
+
+def test_smoothing_factor_edge_values():
+    ax = np.array([0, 4, 1, 0, 3.5e38, 1e-38, 7], F32)
+    aw = np.array([1, 1, 0, 0, 1e-3, 1e3, 7], F32)
+    s = host(W.w8a8_smoothing_factors(dev(ax), dev(aw)))
+    torch().cuda.synchronize()
+    np.testing.assert_array_equal(s.view(np.uint32), O.smoothing_factors(ax, aw).view(np.uint32))
+
+
+# ---------------------------------------------------------------------------
+# whole linear
+# ---------------------------------------------------------------------------
+
+LIN_SHAPES = [(1, 64, 4096), (16, 4096, 4096), (17, 300, 1040), (64, 1024, 14336),
+              (65, 512, 2048), (300, 700, 4096)]
+
+
+@pytest.mark.parametrize("M,N,K", LIN_SHAPES, ids=[f"M{m}_N{n}_K{k}" for m, n, k in LIN_SHAPES])
+def test_linear_against_oracle(M, N, K):
+    x = act(M, K, "lin")
+    w = WL.weights(N, K, 0.02, "lin")
+    # each side prepares its own weights from the same bf16 inputs
+    s_ref = smooth_for(x, w)
+    wq_ref, sw_ref = O.prepare_weight(w, s_ref)
+    ref = O.linear(x, s_ref, wq_ref, sw_ref)
+    xd, wd = dev_bf16(x), dev_bf16(w)
+    s = W.w8a8_smoothing_factors(W.w8a8_channel_absmax(xd), W.w8a8_channel_absmax(wd))
+    wq, sw = W.w8a8_quantize_weight(wd, s)
+    y = W.w8a8_linear(xd, s, wq, sw)
+    xq, st = W.w8a8_quantize_act(xd, s)
+    acc = W.w8a8_gemm_i32(xq, wq)
+    torch().cuda.synchronize()
+    np.testing.assert_array_equal(host(xq), ref["xq"])
+    np.testing.assert_array_equal(host(st), ref["s_tok"])
+    np.testing.assert_array_equal(host(acc), ref["acc"])
+    check_bf16(host(y), ref["y64"], ref["y"])
+
+
+def test_linear_single_workload_full():
+    """The 16-token 4096x4096 layer, every output compared."""
+    wl = WL.WORKLOADS["single"]
+    (proj, N, K), M = wl.shapes[0], wl.ms[0]
+    x, w = WL.layer_inputs(wl, proj, N, K, M)
+    s_ref = smooth_for(x, w)
+    wq_ref, sw_ref = O.prepare_weight(w, s_ref)
+    ref = O.linear(x, s_ref, wq_ref, sw_ref)
+    xd, wd = dev_bf16(x), dev_bf16(w)
+    s = W.w8a8_smoothing_factors(W.w8a8_channel_absmax(xd), W.w8a8_channel_absmax(wd))
+    wq, sw = W.w8a8_quantize_weight(wd, s)
+    ws = torch().empty(W.w8a8_linear_workspace_bytes(M, K), dtype=torch().uint8, device="cuda")
+    y = W.w8a8_linear(xd, s, wq, sw, workspace=ws)
+    torch().cuda.synchronize()
+    np.testing.assert_array_equal(host(wq), wq_ref)
+    check_bf16(host(y), ref["y64"], ref["y"])
+
+
+def test_linear_reads_strided_input_slice():
+    """o_proj consuming the first 4096 columns of a qkv-shaped [M, 6144] output."""
+    M, K, N = 24, 4096, 512
+    big = act(M, 6144, "slice")
+    w = WL.weights(N, K, 0.02, "slice")
+    xs = big[:, :K]
+    s_ref = smooth_for(xs, w)
+    wq_ref, sw_ref = O.prepare_weight(w, s_ref)
+    ref = O.linear(xs, s_ref, wq_ref, sw_ref)
+    xd = dev_bf16(big)[:, :K]
+    wd = dev_bf16(w)
+    s = W.w8a8_smoothing_factors(W.w8a8_channel_absmax(xd), W.w8a8_channel_absmax(wd))
+    wq, sw = W.w8a8_quantize_weight(wd, s)
+    y = W.w8a8_linear(xd, s, wq, sw)
+    torch().cuda.synchronize()
+    check_bf16(host(y), ref["y64"], ref["y"])
