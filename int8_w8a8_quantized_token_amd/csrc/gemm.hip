@@ -41,15 +41,15 @@ __device__ __forceinline__ float dequant(int acc, float st, float sc) {
   return ((float)acc * st) * sc;
 }
 
-// Writes 4 consecutive outputs of row m starting at column n (n % 4 == 0).
+// Writes 4 consecutive outputs of row m starting at column n (n % 4 == 0):
+// int32 accumulators, or bf16((float(acc) * st) * sc[e]).
 // vec: the output rows allow one 8-byte (bf16) or 16-byte (int32) store
 // per group of 4 (checked on the host: base and row stride aligned).
 template <bool I32OUT>
 __device__ __forceinline__ void store4(uint16_t* __restrict__ y, int64_t ldy,
-                                       int32_t* __restrict__ c, int64_t ldc,
-                                       const float* __restrict__ s_tok,
-                                       const float* __restrict__ s_chan, int m, int n, int N,
-                                       bool vec, int a0, int a1, int a2, int a3) {
+                                       int32_t* __restrict__ c, int64_t ldc, int m, int n, int N,
+                                       bool vec, float st, const float (&sc)[4], int a0, int a1,
+                                       int a2, int a3) {
   if constexpr (I32OUT) {
     int32_t* p = c + (int64_t)m * ldc + n;
     if (vec && n + 3 < N) {
@@ -59,60 +59,89 @@ __device__ __forceinline__ void store4(uint16_t* __restrict__ y, int64_t ldy,
       for (int e = 0; e < 4 && n + e < N; ++e) p[e] = a[e];
     }
   } else {
-    const float st = s_tok[m];
     uint16_t* p = y + (int64_t)m * ldy + n;
+    const uint32_t b0 = f32_to_bf16_rne(dequant(a0, st, sc[0]));
+    const uint32_t b1 = f32_to_bf16_rne(dequant(a1, st, sc[1]));
+    const uint32_t b2 = f32_to_bf16_rne(dequant(a2, st, sc[2]));
+    const uint32_t b3 = f32_to_bf16_rne(dequant(a3, st, sc[3]));
     if (vec && n + 3 < N) {
-      const uint32_t b0 = f32_to_bf16_rne(dequant(a0, st, s_chan[n]));
-      const uint32_t b1 = f32_to_bf16_rne(dequant(a1, st, s_chan[n + 1]));
-      const uint32_t b2 = f32_to_bf16_rne(dequant(a2, st, s_chan[n + 2]));
-      const uint32_t b3 = f32_to_bf16_rne(dequant(a3, st, s_chan[n + 3]));
       *reinterpret_cast<uint2*>(p) = uint2{b0 | (b1 << 16), b2 | (b3 << 16)};
     } else {
-      const int a[4] = {a0, a1, a2, a3};
-      for (int e = 0; e < 4 && n + e < N; ++e)
-        p[e] = (uint16_t)f32_to_bf16_rne(dequant(a[e], st, s_chan[n + e]));
+      const uint32_t b[4] = {b0, b1, b2, b3};
+      for (int e = 0; e < 4 && n + e < N; ++e) p[e] = (uint16_t)b[e];
     }
   }
 }
 
+// Loads the 4 channel scales of outputs n..n+3 (clamped to valid indices;
+// values for columns past N are never stored).
+__device__ __forceinline__ void load_chan4(const float* __restrict__ s_chan, int n, int N,
+                                           float (&sc)[4]) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) sc[e] = s_chan[min(n + e, N - 1)];
+}
+
 // ---------------------------------------------------------------------------
-// Skinny kernel: M <= 16*MT tokens, 16 output channels per workgroup.
+// Skinny kernel (decode): M <= 16*MT tokens. A workgroup owns 16*RW output
+// channels; its NW waves take interleaved 64-byte K chunks, U chunks in
+// flight per wave. Each token fragment is reused for RW weight fragments and
+// each weight fragment for MT token fragments.
 // ---------------------------------------------------------------------------
 
-constexpr int kSkinnyWaves = 8;
-constexpr int kSkinnyUnroll = 8;
+template <int MT, int RW, int NW, int U>
+struct SkinnyCfg {
+  static constexpr int kThreads = NW * kWave;
+  static constexpr int kRows = 16 * RW;
+  static_assert(MT >= 1 && MT <= 4 && RW >= 1 && NW >= 1 && U >= 1, "");
+  static_assert(NW * RW * MT <= 64, "LDS reduction buffer at most 64 KB");
+};
 
-template <int MT, bool I32OUT>
-__global__ __launch_bounds__(kSkinnyWaves * kWave) void gemm_skinny_kernel(
+template <int MT, int RW, int NW, int U, bool I32OUT>
+__global__ __launch_bounds__(NW * kWave) void gemm_skinny_kernel(
     const int8_t* __restrict__ xq, int64_t ldq, const float* __restrict__ s_tok,
     const int8_t* __restrict__ wq, int64_t ldw, const float* __restrict__ s_chan, int M, int N,
     int K, uint16_t* __restrict__ y, int64_t ldy, int32_t* __restrict__ c, int64_t ldc,
     bool vec_out) {
-  constexpr int NW = kSkinnyWaves, U = kSkinnyUnroll;
-  __shared__ v4i red[NW][MT][kWave];
+  __shared__ v4i red[NW][RW * MT][kWave];
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int r = lane & 15, g = lane >> 4;
-  const int n0 = blockIdx.x * 16;
+  const int n0 = blockIdx.x * 16 * RW;
 
   // Rows past N or M read a valid row; their results land only in outputs
   // that are never stored, since D[i][j] depends on A row i and B row j only.
-  const int8_t* wp = wq + (int64_t)min(n0 + r, N - 1) * ldw + g * 16;
+  const int8_t* wp[RW];
+#pragma unroll
+  for (int rw = 0; rw < RW; ++rw) wp[rw] = wq + (int64_t)min(n0 + 16 * rw + r, N - 1) * ldw + g * 16;
   const int8_t* xp[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) xp[mt] = xq + (int64_t)min(mt * 16 + r, M - 1) * ldq + g * 16;
 
-  v4i acc[MT];
+  // Epilogue scales, fetched before the weight stream so that their latency
+  // hides under it.
+  float st[MT], sc[RW][4];
+  if constexpr (!I32OUT) {
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt] = v4i{0, 0, 0, 0};
+    for (int mt = 0; mt < MT; ++mt) st[mt] = s_tok[min(mt * 16 + r, M - 1)];
+#pragma unroll
+    for (int rw = 0; rw < RW; ++rw) load_chan4(s_chan, n0 + 16 * rw + 4 * g, N, sc[rw]);
+  }
+
+  v4i acc[RW][MT];
+#pragma unroll
+  for (int rw = 0; rw < RW; ++rw)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[rw][mt] = v4i{0, 0, 0, 0};
 
   const int nfull = K / 64;
   int ch = wave;
   for (; ch + (U - 1) * NW < nfull; ch += U * NW) {
-    v4i b[U], a[U][MT];
+    v4i b[U][RW], a[U][MT];
 #pragma unroll
-    for (int u = 0; u < U; ++u) b[u] = ldg16(wp + (int64_t)(ch + u * NW) * 64);
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int rw = 0; rw < RW; ++rw) b[u][rw] = ldg16(wp[rw] + (int64_t)(ch + u * NW) * 64);
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -120,44 +149,65 @@ __global__ __launch_bounds__(kSkinnyWaves * kWave) void gemm_skinny_kernel(
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        acc[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(b[u], a[u][mt], acc[mt], 0, 0, 0);
+      for (int rw = 0; rw < RW; ++rw)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          acc[rw][mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(b[u][rw], a[u][mt], acc[rw][mt], 0, 0, 0);
   }
   for (; ch < nfull; ch += NW) {
-    const v4i b = ldg16(wp + (int64_t)ch * 64);
+    v4i b[RW], a[MT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-      acc[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(b, ldg16(xp[mt] + (int64_t)ch * 64), acc[mt],
-                                                      0, 0, 0);
+    for (int rw = 0; rw < RW; ++rw) b[rw] = ldg16(wp[rw] + (int64_t)ch * 64);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) a[mt] = ldg16(xp[mt] + (int64_t)ch * 64);
+#pragma unroll
+    for (int rw = 0; rw < RW; ++rw)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        acc[rw][mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(b[rw], a[mt], acc[rw][mt], 0, 0, 0);
   }
   // K % 64 in {16, 32, 48}: the last chunk is partial; groups past K are zero.
   const int tail = K - nfull * 64;
   if (tail > 0 && wave == nfull % NW) {
     const bool in = g * 16 < tail;
     const v4i zero = {0, 0, 0, 0};
-    const v4i b = in ? ldg16(wp + (int64_t)nfull * 64) : zero;
+    v4i b[RW], a[MT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const v4i a = in ? ldg16(xp[mt] + (int64_t)nfull * 64) : zero;
-      acc[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(b, a, acc[mt], 0, 0, 0);
-    }
+    for (int rw = 0; rw < RW; ++rw) b[rw] = in ? ldg16(wp[rw] + (int64_t)nfull * 64) : zero;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) a[mt] = in ? ldg16(xp[mt] + (int64_t)nfull * 64) : zero;
+#pragma unroll
+    for (int rw = 0; rw < RW; ++rw)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        acc[rw][mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(b[rw], a[mt], acc[rw][mt], 0, 0, 0);
   }
 
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) red[wave][mt][lane] = acc[mt];
+  for (int rw = 0; rw < RW; ++rw)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) red[wave][rw * MT + mt][lane] = acc[rw][mt];
   __syncthreads();
 
-  // Wave w finishes token tile w (MT <= NW).
-  if (wave < MT) {
-    const int mt = wave;
-    v4i sum = red[0][mt][lane];
+  // Tile t = rw * MT + mt is finished by wave t % NW: sum the NW partial
+  // tiles, then lane l holds token m = 16 mt + l % 16 and the 4 output
+  // channels 16 rw + 4 (l / 16) + e.
 #pragma unroll
-    for (int w = 1; w < NW; ++w) sum += red[w][mt][lane];
-    const int m = mt * 16 + r;
-    const int n = n0 + 4 * g;
-    if (m < M && n < N) store4<I32OUT>(y, ldy, c, ldc, s_tok, s_chan, m, n, N, vec_out, sum[0], sum[1],
-                                  sum[2], sum[3]);
-  }
+  for (int rw = 0; rw < RW; ++rw)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      if ((rw * MT + mt) % NW != wave) continue;
+      v4i sum = red[0][rw * MT + mt][lane];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) sum += red[w][rw * MT + mt][lane];
+      const int m = mt * 16 + r;
+      const int n = n0 + 16 * rw + 4 * g;
+      if (m < M && n < N) {
+        const float stm = I32OUT ? 0.0f : st[mt];
+        store4<I32OUT>(y, ldy, c, ldc, m, n, N, vec_out, stm, sc[rw], sum[0], sum[1], sum[2],
+                       sum[3]);
+      }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -281,14 +331,225 @@ __global__ __launch_bounds__(WN * WM * kWave) void gemm_tiled_kernel(
     for (int j = 0; j < FM; ++j) {
       const int m = m0 + wm * FM * 32 + j * 32 + (lane & 31);
       if (m >= M) continue;
+      const float st = I32OUT ? 0.0f : s_tok[m];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int n = n0 + wn * FN * 32 + i * 32 + 8 * q + 4 * (lane >> 5);
-        if (n < N)
-          store4<I32OUT>(y, ldy, c, ldc, s_tok, s_chan, m, n, N, vec_out, acc[i][j][4 * q],
+        if (n < N) {
+          float sc[4] = {0, 0, 0, 0};
+          if constexpr (!I32OUT) load_chan4(s_chan, n, N, sc);
+          store4<I32OUT>(y, ldy, c, ldc, m, n, N, vec_out, st, sc, acc[i][j][4 * q],
                          acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+        }
       }
     }
+}
+
+// ---------------------------------------------------------------------------
+// Prefill kernel: 256 x 256 output tile per workgroup, BK = 64 bytes of K per
+// stage, NS LDS stages fed by direct global -> LDS loads
+// (global_load_lds_dwordx4), 4 waves in a 2 x 2 grid, each owning a
+// 128 x 128 sub-tile as 4 x 4 v_mfma_i32_32x32x32_i8 fragments (256
+// accumulator registers per lane, held in AGPRs).
+//
+// LDS layout of a stage: W tile [256 rows][64 B] then X tile [256][64 B].
+// Row r's 16-byte chunk c sits at chunk slot c ^ swz(r),
+// swz(r) = ((r >> 1) ^ (r >> 2)) & 3, so the 32 rows one fragment read
+// touches spread over all banks (conflict-free for 8-lane/32-bank and
+// 16-lane/64-bank service alike). A DMA instruction writes 64 consecutive
+// chunks (1 KB) of LDS; the swizzle is applied by choosing which global
+// chunk each lane fetches.
+//
+// Pipeline per stage s: wait for this wave's DMA of stage s (vmcnt), one
+// s_barrier (all waves' DMA of stage s landed, all reads of stage s-1 done),
+// issue the DMA of stage s + NS - 1 into the buffer stage s - 1 used, then
+// run stage s's ds_reads and MFMAs. The barrier is a bare s_barrier: a
+// fence would wait for every outstanding DMA and serialize the stages.
+// Each stage buffer is its own __shared__ array so the compiler knows that
+// reading one buffer does not depend on DMA into another.
+// ---------------------------------------------------------------------------
+
+namespace pf {
+constexpr int TN = 256, TM = 256, BK = 64, NS = 4, THREADS = 256;
+constexpr int TILE_BYTES = TN * BK;               // 16 KB per operand per stage
+constexpr int STAGE_BYTES = 2 * TILE_BYTES;       // W then X
+constexpr int DMA_PER_OPERAND = TILE_BYTES / (THREADS * 16);   // 4 per wave
+constexpr int DMA_PER_STAGE = 2 * DMA_PER_OPERAND;              // 8 per wave
+constexpr int GROUP_M = 4;                        // M tiles per tile group
+}  // namespace pf
+
+__device__ __forceinline__ int lds_swz(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
+
+// s_waitcnt with vmcnt = n and the other counters left alone (gfx9 encoding).
+#define W8A8_WAIT_VM(n) \
+  __builtin_amdgcn_s_waitcnt(((n) & 0xF) | ((((n) >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8))
+
+__device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::: "memory"); }
+
+#define W8A8_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+template <bool I32OUT>
+__global__ __launch_bounds__(pf::THREADS, 1) void gemm_prefill_kernel(
+    const int8_t* __restrict__ xq, int64_t ldq, const float* __restrict__ s_tok,
+    const int8_t* __restrict__ wq, int64_t ldw, const float* __restrict__ s_chan, int M, int N,
+    int K, uint16_t* __restrict__ y, int64_t ldy, int32_t* __restrict__ c, int64_t ldc,
+    bool vec_out) {
+  using namespace pf;
+  __shared__ __attribute__((aligned(1024))) int8_t buf0[STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) int8_t buf1[STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) int8_t buf2[STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) int8_t buf3[STAGE_BYTES];
+  static_assert(NS == 4, "four stage buffers are declared");
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int wn = wave & 1, wm = wave >> 1;
+
+  // ---- tile index: XCD-aware, then grouped along M ----
+  const int tiles_n = (N + TN - 1) / TN, tiles_m = (M + TM - 1) / TM;
+  const int T = tiles_n * tiles_m;
+  const int b = blockIdx.x;
+  const int Tq = T / 8;
+  // workgroups are dealt round-robin to the 8 XCDs: give each XCD a run of
+  // consecutive tiles so that its L2 sees shared W and X panels
+  const int t = (b < 8 * Tq) ? (b % 8) * Tq + b / 8 : b;
+  const int group = t / (GROUP_M * tiles_n);
+  const int first_m = group * GROUP_M;
+  const int gsize = min(tiles_m - first_m, GROUP_M);
+  const int in_group = t % (GROUP_M * tiles_n);
+  const int tile_m = first_m + in_group % gsize;
+  const int tile_n = in_group / gsize;
+  const int n0 = tile_n * TN, m0 = tile_m * TM;
+
+  // ---- DMA sources: instruction i of this wave fills LDS chunks
+  // [i*256 + wave*64, +64); chunk p holds row p/4, global chunk (p%4)^swz ----
+  const int8_t* wsrc[DMA_PER_OPERAND];
+  const int8_t* xsrc[DMA_PER_OPERAND];
+#pragma unroll
+  for (int i = 0; i < DMA_PER_OPERAND; ++i) {
+    const int p = i * THREADS + wave * kWave + lane;
+    const int row = p >> 2, cidx = (p & 3) ^ lds_swz(p >> 2);
+    wsrc[i] = wq + (int64_t)min(n0 + row, N - 1) * ldw + cidx * 16;
+    xsrc[i] = xq + (int64_t)min(m0 + row, M - 1) * ldq + cidx * 16;
+  }
+  auto issue = [&](int stage, int8_t* bufp) {
+    const int64_t k0 = (int64_t)stage * BK;
+#pragma unroll
+    for (int i = 0; i < DMA_PER_OPERAND; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(wsrc[i] + k0),
+                                       W8A8_LDS(bufp + (i * THREADS + wave * kWave) * 16), 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < DMA_PER_OPERAND; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(xsrc[i] + k0),
+                                       W8A8_LDS(bufp + TILE_BYTES + (i * THREADS + wave * kWave) * 16),
+                                       16, 0, 0);
+  };
+
+  // ---- fragment read offsets: row (l % 32) of a fragment, K chunk 2ks + l/32 ----
+  const int frow = lane & 31;
+  const int sw = lds_swz(frow);           // fragment bases are multiples of 32 rows
+  int foff[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) foff[ks] = frow * BK + (((2 * ks + (lane >> 5)) ^ sw) << 4);
+  const int wbase = wn * 128 * BK, xbase = TILE_BYTES + wm * 128 * BK;
+
+  v16i acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
+
+  auto compute = [&](const int8_t* bufp) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      v4i a[4], bb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        a[i] = *reinterpret_cast<const v4i*>(bufp + wbase + i * 32 * BK + foff[ks]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        bb[j] = *reinterpret_cast<const v4i*>(bufp + xbase + j * 32 * BK + foff[ks]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], bb[j], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  const int nfull = K / BK;
+  if (0 < nfull) issue(0, buf0);
+  if (1 < nfull) issue(1, buf1);
+  if (2 < nfull) issue(2, buf2);
+
+#define W8A8_PF_STAGE(J, CUR, NEXT)                                  \
+  {                                                                  \
+    const int st = s0 + (J);                                         \
+    if (st < nfull) {                                                \
+      if (st + NS - 2 < nfull) W8A8_WAIT_VM((NS - 2) * DMA_PER_STAGE); \
+      else W8A8_WAIT_VM(0);                                          \
+      barrier_no_fence();                                            \
+      if (st + NS - 1 < nfull) issue(st + NS - 1, NEXT);             \
+      compute(CUR);                                                  \
+    }                                                                \
+  }
+  for (int s0 = 0; s0 < nfull; s0 += NS) {
+    W8A8_PF_STAGE(0, buf0, buf3)
+    W8A8_PF_STAGE(1, buf1, buf0)
+    W8A8_PF_STAGE(2, buf2, buf1)
+    W8A8_PF_STAGE(3, buf3, buf2)
+  }
+#undef W8A8_PF_STAGE
+
+  // ---- K tail (K % 64 in {16, 32, 48}): staged through registers with
+  // zero fill into the buffer the next stage would use ----
+  if (nfull * BK < K) {
+    int8_t* tb = (nfull % NS == 0) ? buf0 : (nfull % NS == 1) ? buf1 : (nfull % NS == 2) ? buf2 : buf3;
+    const int64_t k0 = (int64_t)nfull * BK;
+    const v4i zero = {0, 0, 0, 0};
+    v4i wv[DMA_PER_OPERAND], xv[DMA_PER_OPERAND];
+#pragma unroll
+    for (int i = 0; i < DMA_PER_OPERAND; ++i) {
+      const int p = i * THREADS + wave * kWave + lane;
+      const int cidx = (p & 3) ^ lds_swz(p >> 2);
+      const bool in = k0 + cidx * 16 < K;
+      wv[i] = in ? ldg16(wsrc[i] + k0) : zero;
+      xv[i] = in ? ldg16(xsrc[i] + k0) : zero;
+    }
+    W8A8_WAIT_VM(0);
+    barrier_no_fence();       // every wave is done reading the buffer about to be refilled
+#pragma unroll
+    for (int i = 0; i < DMA_PER_OPERAND; ++i) {
+      *reinterpret_cast<v4i*>(tb + (i * THREADS + wave * kWave + lane) * 16) = wv[i];
+      *reinterpret_cast<v4i*>(tb + TILE_BYTES + (i * THREADS + wave * kWave + lane) * 16) = xv[i];
+    }
+    __syncthreads();
+    compute(tb);
+  }
+
+  // ---- epilogue: lane holds token m = .. + l % 32 and, per group of 4
+  // registers, four consecutive output channels ----
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int m = m0 + wm * 128 + j * 32 + (lane & 31);
+    if (m >= M) continue;
+    const float st = I32OUT ? 0.0f : s_tok[m];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = n0 + wn * 128 + i * 32 + 8 * q + 4 * (lane >> 5);
+        if (n < N) {
+          float sc[4] = {0, 0, 0, 0};
+          if constexpr (!I32OUT) load_chan4(s_chan, n, N, sc);
+          store4<I32OUT>(y, ldy, c, ldc, m, n, N, vec_out, st, sc, acc[i][j][4 * q],
+                         acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+        }
+      }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -296,6 +557,17 @@ __global__ __launch_bounds__(WN * WM * kWave) void gemm_tiled_kernel(
 // ---------------------------------------------------------------------------
 
 constexpr int kSkinnyMaxM = 64;
+constexpr int kPrefillMinM = 512;
+
+template <int MT, int RW, int NW, int U, bool I32OUT>
+static void launch_skinny(const int8_t* xq, int64_t ldq, const float* s_tok, const int8_t* wq,
+                          int64_t ldw, const float* s_chan, int M, int N, int K, uint16_t* y,
+                          int64_t ldy, int32_t* c, int64_t ldc, bool vec_out, hipStream_t s) {
+  using C = SkinnyCfg<MT, RW, NW, U>;
+  const dim3 grid((unsigned)((N + C::kRows - 1) / C::kRows)), block(C::kThreads);
+  hipLaunchKernelGGL((gemm_skinny_kernel<MT, RW, NW, U, I32OUT>), grid, block, 0, s, xq, ldq,
+                     s_tok, wq, ldw, s_chan, M, N, K, y, ldy, c, ldc, vec_out);
+}
 
 template <bool I32OUT>
 static hipError_t launch_gemm_t(const int8_t* xq, int64_t ldq, const float* s_tok,
@@ -303,15 +575,40 @@ static hipError_t launch_gemm_t(const int8_t* xq, int64_t ldq, const float* s_to
                                 int N, int K, uint16_t* y, int64_t ldy, int32_t* c, int64_t ldc,
                                 bool vec_out, hipStream_t s) {
   if (M <= kSkinnyMaxM) {
-    const dim3 grid((unsigned)((N + 15) / 16)), block(kSkinnyWaves * kWave);
-#define W8A8_SKINNY(MTV)                                                                    \
-  hipLaunchKernelGGL((gemm_skinny_kernel<MTV, I32OUT>), grid, block, 0, s, xq, ldq, s_tok, wq, \
-                     ldw, s_chan, M, N, K, y, ldy, c, ldc, vec_out)
-    if (M <= 16) W8A8_SKINNY(1);
-    else if (M <= 32) W8A8_SKINNY(2);
-    else if (M <= 48) W8A8_SKINNY(3);
-    else W8A8_SKINNY(4);
+#define W8A8_SKINNY(MTV, RWV, NWV, UV)                                                       \
+  launch_skinny<MTV, RWV, NWV, UV, I32OUT>(xq, ldq, s_tok, wq, ldw, s_chan, M, N, K, y, ldy, c, \
+                                           ldc, vec_out, s)
+    // Shape classes measured on MI355X (Llama-3.1-8B projection shapes). More
+    // weight rows per wave (RW) reuse each token fragment more often but
+    // leave fewer workgroups; they pay off once N is large or M > 16.
+    const bool wide = N > 8192, mid = N > 4096 && N <= 8192, deep = K > 8192;
+    if (M <= 4) {
+      if (mid) W8A8_SKINNY(1, 2, 8, 8);
+      else W8A8_SKINNY(1, 1, 16, 8);
+    } else if (M <= 16) {
+      if (wide) W8A8_SKINNY(1, 4, 8, 2);
+      else if (mid) W8A8_SKINNY(1, 2, 8, 8);
+      else if (deep) W8A8_SKINNY(1, 1, 8, 4);
+      else W8A8_SKINNY(1, 1, 16, 8);
+    } else if (M <= 32) {
+      if (wide) W8A8_SKINNY(2, 4, 4, 2);
+      else if (mid) W8A8_SKINNY(2, 2, 8, 4);
+      else W8A8_SKINNY(2, 1, 16, 4);
+    } else if (M <= 48) {
+      if (wide) W8A8_SKINNY(3, 4, 4, 2);
+      else if (mid) W8A8_SKINNY(3, 2, 8, 2);
+      else W8A8_SKINNY(3, 1, 16, 2);
+    } else {
+      if (wide) W8A8_SKINNY(4, 4, 4, 2);
+      else if (mid) W8A8_SKINNY(4, 2, 8, 2);
+      else if (deep) W8A8_SKINNY(4, 1, 16, 2);
+      else W8A8_SKINNY(4, 1, 8, 8);
+    }
 #undef W8A8_SKINNY
+  } else if (M >= kPrefillMinM) {
+    const int tiles = ((N + pf::TN - 1) / pf::TN) * ((M + pf::TM - 1) / pf::TM);
+    hipLaunchKernelGGL((gemm_prefill_kernel<I32OUT>), dim3((unsigned)tiles), dim3(pf::THREADS), 0, s,
+                       xq, ldq, s_tok, wq, ldw, s_chan, M, N, K, y, ldy, c, ldc, vec_out);
   } else {
     constexpr int TN = 128, TM = 128, BK = 64, WN = 2, WM = 2;
     const dim3 grid((unsigned)((N + TN - 1) / TN), (unsigned)((M + TM - 1) / TM));

@@ -12,11 +12,12 @@
 // Codes round half away from zero and are clamped to [-127, 127] (the worked
 // example of "How SmoothQuant prevents outliers in activation tensors").
 //
-// Design (HBM-bound): one 256-thread workgroup per row; each thread reads
-// 16-byte vectors (8 bf16) at stride 256 vectors, so a wavefront reads 1 KB
-// contiguous per load. The row stays in registers between the absmax pass and
-// the quantize pass (rows up to 32768 channels), so HBM sees each input byte
-// once and each output byte once. Every floating-point step is one correctly
+// Design (HBM-bound): one workgroup per row (1024 threads when there are few
+// rows, 256 otherwise); each thread reads 16-byte vectors (8 bf16) at a
+// stride of one block, so a wavefront reads 1 KB contiguous per load. The row
+// stays in registers between the absmax pass and the quantize pass (rows up
+// to 32768 channels), so HBM sees each input byte once and each output byte
+// once. Every floating-point step is one correctly
 // rounded binary32 operation in the order written (no contraction, true
 // divisions), which is what makes the codes bit-exact.
 
@@ -25,7 +26,9 @@
 
 namespace w8a8 {
 
-constexpr int kRowThreads = 256;
+constexpr int kRowThreads = 256;      // threads per row, large M
+constexpr int kRowThreadsSmallM = 1024; // threads per row when few rows fill the chip
+constexpr int64_t kSmallM = 512;
 
 template <RowMode MODE, bool SMOOTH>
 __device__ __forceinline__ float prep_value(float v, const float* __restrict__ smooth, int k) {
@@ -63,6 +66,7 @@ __device__ __forceinline__ void store_codes8(int8_t* __restrict__ qr, int vi, co
 }
 
 // Block-wide max of nonnegative values; every thread gets the result.
+template <int BS>
 __device__ __forceinline__ float block_max(float v, float* red) {
   v = wave_max(v);
   const int wave = threadIdx.x / kWave;
@@ -70,17 +74,18 @@ __device__ __forceinline__ float block_max(float v, float* red) {
   __syncthreads();
   float r = red[0];
 #pragma unroll
-  for (int w = 1; w < kRowThreads / kWave; ++w) r = fmaxf(r, red[w]);
+  for (int w = 1; w < BS / kWave; ++w) r = fmaxf(r, red[w]);
   return r;
 }
 
-// NV > 0: each thread keeps NV vectors in registers (K <= NV * 2048).
+// One BS-thread workgroup per row.
+// NV > 0: each thread keeps NV vectors in registers (K <= NV * 8 * BS).
 // NV == 0: rows longer than that are read twice (second read hits L2).
-template <int NV, RowMode MODE, bool SMOOTH>
-__global__ __launch_bounds__(kRowThreads) void quantize_rows_kernel(
+template <int BS, int NV, RowMode MODE, bool SMOOTH>
+__global__ __launch_bounds__(BS) void quantize_rows_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const float* __restrict__ smooth, int K,
     int8_t* __restrict__ q, int64_t ldq, float* __restrict__ scale) {
-  __shared__ float red[kRowThreads / kWave];
+  __shared__ float red[BS / kWave];
   const int64_t row = blockIdx.x;
   const uint16_t* xr = x + row * ldx;
   int8_t* qr = q + row * ldq;
@@ -92,33 +97,33 @@ __global__ __launch_bounds__(kRowThreads) void quantize_rows_kernel(
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      const int vi = tid + i * kRowThreads;
+      const int vi = tid + i * BS;
       if (vi < nvec) {
         load_prep8<MODE, SMOOTH>(xr, smooth, vi, v[i]);
 #pragma unroll
         for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[i][e]));
       }
     }
-    amax = block_max(amax, red);
+    amax = block_max<BS>(amax, red);
     const float S = amax / kQMax;
     if (tid == 0) scale[row] = S;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      const int vi = tid + i * kRowThreads;
+      const int vi = tid + i * BS;
       if (vi < nvec) store_codes8(qr, vi, v[i], S);
     }
   } else {
     float amax = 0.0f;
-    for (int vi = tid; vi < nvec; vi += kRowThreads) {
+    for (int vi = tid; vi < nvec; vi += BS) {
       float v[8];
       load_prep8<MODE, SMOOTH>(xr, smooth, vi, v);
 #pragma unroll
       for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
     }
-    amax = block_max(amax, red);
+    amax = block_max<BS>(amax, red);
     const float S = amax / kQMax;
     if (tid == 0) scale[row] = S;
-    for (int vi = tid; vi < nvec; vi += kRowThreads) {
+    for (int vi = tid; vi < nvec; vi += BS) {
       float v[8];
       load_prep8<MODE, SMOOTH>(xr, smooth, vi, v);
       store_codes8(qr, vi, v, S);
@@ -126,24 +131,42 @@ __global__ __launch_bounds__(kRowThreads) void quantize_rows_kernel(
   }
 }
 
-template <RowMode MODE, bool SMOOTH>
-static hipError_t launch_rows_nv(const uint16_t* x, int64_t ldx, const float* smooth,
-                                 int64_t rows, int64_t K, int8_t* q, int64_t ldq,
-                                 float* scale, hipStream_t s) {
-  const int64_t per_thread = (K / 8 + kRowThreads - 1) / kRowThreads;
-  const dim3 grid((unsigned)rows), block(kRowThreads);
+template <int BS, RowMode MODE, bool SMOOTH>
+static hipError_t launch_rows_bs(const uint16_t* x, int64_t ldx, const float* smooth,
+                                 int64_t rows, int64_t K, int8_t* q, int64_t ldq, float* scale,
+                                 hipStream_t s) {
+  const int64_t per_thread = (K / 8 + BS - 1) / BS;
+  const dim3 grid((unsigned)rows), block(BS);
   const int k = (int)K;
-#define W8A8_LAUNCH_NV(NVV)                                                                 \
-  hipLaunchKernelGGL((quantize_rows_kernel<NVV, MODE, SMOOTH>), grid, block, 0, s, x, ldx, \
+#define W8A8_LAUNCH_NV(NVV)                                                                    \
+  hipLaunchKernelGGL((quantize_rows_kernel<BS, NVV, MODE, SMOOTH>), grid, block, 0, s, x, ldx, \
                      smooth, k, q, ldq, scale)
   if (per_thread <= 1) W8A8_LAUNCH_NV(1);
   else if (per_thread <= 2) W8A8_LAUNCH_NV(2);
   else if (per_thread <= 4) W8A8_LAUNCH_NV(4);
   else if (per_thread <= 8) W8A8_LAUNCH_NV(8);
-  else if (per_thread <= 16) W8A8_LAUNCH_NV(16);
-  else W8A8_LAUNCH_NV(0);
+  else {
+    if constexpr (BS == kRowThreads) {
+      if (per_thread <= 16) {
+        W8A8_LAUNCH_NV(16);
+        return hipGetLastError();
+      }
+    }
+    W8A8_LAUNCH_NV(0);
+  }
 #undef W8A8_LAUNCH_NV
   return hipGetLastError();
+}
+
+// Few rows cannot fill the chip, so each row gets 1024 threads (shorter
+// per-thread chains of divisions); many rows use 256 threads per row.
+template <RowMode MODE, bool SMOOTH>
+static hipError_t launch_rows_nv(const uint16_t* x, int64_t ldx, const float* smooth,
+                                 int64_t rows, int64_t K, int8_t* q, int64_t ldq, float* scale,
+                                 hipStream_t s) {
+  if (rows <= kSmallM)
+    return launch_rows_bs<kRowThreadsSmallM, MODE, SMOOTH>(x, ldx, smooth, rows, K, q, ldq, scale, s);
+  return launch_rows_bs<kRowThreads, MODE, SMOOTH>(x, ldx, smooth, rows, K, q, ldq, scale, s);
 }
 
 hipError_t launch_quantize_rows(RowMode mode, const uint16_t* x, int64_t ldx,

@@ -115,6 +115,9 @@ GEMM_SHAPES = [
     # tiled path
     (65, 1, 16), (65, 128, 64), (100, 129, 112), (128, 256, 4096), (130, 300, 1040),
     (257, 515, 208), (512, 512, 2048), (1000, 384, 4096 + 48),
+    # prefill path (M >= 512): 0..3 full 64-byte stages, K tails, ragged M/N
+    (512, 256, 48), (512, 256, 64), (513, 257, 128), (600, 300, 192), (700, 520, 208),
+    (1024, 768, 14336 + 16), (2048, 1000, 1024),
 ]
 
 
