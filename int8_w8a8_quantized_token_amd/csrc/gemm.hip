@@ -370,11 +370,9 @@ __global__ __launch_bounds__(WN * WM * kWave) void gemm_tiled_kernel(
 // ---------------------------------------------------------------------------
 
 namespace pf {
-constexpr int TN = 256, TM = 256, BK = 64, NS = 4, THREADS = 256;
+constexpr int TN = 256, TM = 256, BK = 64, NS = 4;
 constexpr int TILE_BYTES = TN * BK;               // 16 KB per operand per stage
 constexpr int STAGE_BYTES = 2 * TILE_BYTES;       // W then X
-constexpr int DMA_PER_OPERAND = TILE_BYTES / (THREADS * 16);   // 4 per wave
-constexpr int DMA_PER_STAGE = 2 * DMA_PER_OPERAND;              // 8 per wave
 constexpr int GROUP_M = 4;                        // M tiles per tile group
 }  // namespace pf
 
@@ -386,15 +384,44 @@ __device__ __forceinline__ int lds_swz(int row) { return ((row >> 1) ^ (row >> 2
 
 __device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::: "memory"); }
 
-#define W8A8_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+// One global_load_lds_dwordx4: each lane's 16 bytes at gptr land in LDS at
+// lds_base + 16 * lane (lds_base is wave-uniform). Issued as inline asm so
+// that the compiler's wait-count pass does not treat it as a pending LDS
+// write (it would otherwise drain every outstanding DMA before the next LDS
+// read); the kernel's explicit vmcnt waits order it instead. No output
+// registers; the address is read at issue.
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gptr), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory", "m0");
+}
 
-template <bool I32OUT>
-__global__ __launch_bounds__(pf::THREADS, 1) void gemm_prefill_kernel(
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void*)p);
+}
+
+// WN x WM waves; wave (wn, wm) owns output channels [wn*TN/WN, +TN/WN) and
+// tokens [wm*TM/WM, +TM/WM) of the tile as FN x FM 32x32 fragments.
+template <int WN, int WM>
+struct PrefillCfg {
+  static constexpr int kThreads = WN * WM * kWave;
+  static constexpr int kFN = pf::TN / WN / 32, kFM = pf::TM / WM / 32;
+  static constexpr int kDmaPerOperand = pf::TILE_BYTES / (kThreads * 16);
+  static constexpr int kDmaPerStage = 2 * kDmaPerOperand;
+  static_assert(kDmaPerOperand * kThreads * 16 == pf::TILE_BYTES, "");
+};
+
+template <int WN, int WM, bool I32OUT>
+__global__ __launch_bounds__(WN * WM * kWave, 1) void gemm_prefill_kernel(
     const int8_t* __restrict__ xq, int64_t ldq, const float* __restrict__ s_tok,
     const int8_t* __restrict__ wq, int64_t ldw, const float* __restrict__ s_chan, int M, int N,
     int K, uint16_t* __restrict__ y, int64_t ldy, int32_t* __restrict__ c, int64_t ldc,
     bool vec_out) {
   using namespace pf;
+  using C = PrefillCfg<WN, WM>;
+  constexpr int THREADS = C::kThreads, FN = C::kFN, FM = C::kFM;
+  constexpr int DPO = C::kDmaPerOperand, DPS = C::kDmaPerStage;
   __shared__ __attribute__((aligned(1024))) int8_t buf0[STAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) int8_t buf1[STAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) int8_t buf2[STAGE_BYTES];
@@ -404,7 +431,7 @@ __global__ __launch_bounds__(pf::THREADS, 1) void gemm_prefill_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
-  const int wn = wave & 1, wm = wave >> 1;
+  const int wn = wave % WN, wm = wave / WN;
 
   // ---- tile index: XCD-aware, then grouped along M ----
   const int tiles_n = (N + TN - 1) / TN, tiles_m = (M + TM - 1) / TM;
@@ -423,11 +450,11 @@ __global__ __launch_bounds__(pf::THREADS, 1) void gemm_prefill_kernel(
   const int n0 = tile_n * TN, m0 = tile_m * TM;
 
   // ---- DMA sources: instruction i of this wave fills LDS chunks
-  // [i*256 + wave*64, +64); chunk p holds row p/4, global chunk (p%4)^swz ----
-  const int8_t* wsrc[DMA_PER_OPERAND];
-  const int8_t* xsrc[DMA_PER_OPERAND];
+  // [i*THREADS + wave*64, +64); chunk p holds row p/4, global chunk (p%4)^swz ----
+  const int8_t* wsrc[DPO];
+  const int8_t* xsrc[DPO];
 #pragma unroll
-  for (int i = 0; i < DMA_PER_OPERAND; ++i) {
+  for (int i = 0; i < DPO; ++i) {
     const int p = i * THREADS + wave * kWave + lane;
     const int row = p >> 2, cidx = (p & 3) ^ lds_swz(p >> 2);
     wsrc[i] = wq + (int64_t)min(n0 + row, N - 1) * ldw + cidx * 16;
@@ -435,15 +462,11 @@ __global__ __launch_bounds__(pf::THREADS, 1) void gemm_prefill_kernel(
   }
   auto issue = [&](int stage, int8_t* bufp) {
     const int64_t k0 = (int64_t)stage * BK;
+    const uint32_t base = lds_addr(bufp) + wave * kWave * 16;
 #pragma unroll
-    for (int i = 0; i < DMA_PER_OPERAND; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(wsrc[i] + k0),
-                                       W8A8_LDS(bufp + (i * THREADS + wave * kWave) * 16), 16, 0, 0);
+    for (int i = 0; i < DPO; ++i) dma16(wsrc[i] + k0, base + i * THREADS * 16);
 #pragma unroll
-    for (int i = 0; i < DMA_PER_OPERAND; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(xsrc[i] + k0),
-                                       W8A8_LDS(bufp + TILE_BYTES + (i * THREADS + wave * kWave) * 16),
-                                       16, 0, 0);
+    for (int i = 0; i < DPO; ++i) dma16(xsrc[i] + k0, base + TILE_BYTES + i * THREADS * 16);
   };
 
   // ---- fragment read offsets: row (l % 32) of a fragment, K chunk 2ks + l/32 ----
@@ -452,30 +475,42 @@ __global__ __launch_bounds__(pf::THREADS, 1) void gemm_prefill_kernel(
   int foff[2];
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) foff[ks] = frow * BK + (((2 * ks + (lane >> 5)) ^ sw) << 4);
-  const int wbase = wn * 128 * BK, xbase = TILE_BYTES + wm * 128 * BK;
+  const int wbase = wn * FN * 32 * BK, xbase = TILE_BYTES + wm * FM * 32 * BK;
 
-  v16i acc[4][4];
+  v16i acc[FN][FM];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < FN; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < FM; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
+
+  // Epilogue scales of this tile (256 channel + 256 token scales), fetched
+  // now so their latency hides under the K loop; parked in LDS at the end.
+  constexpr int kScalesPerThread = (TN + TM) / THREADS;
+  float scale_pre[kScalesPerThread];
+  if constexpr (!I32OUT) {
+#pragma unroll
+    for (int r = 0; r < kScalesPerThread; ++r) {
+      const int idx = tid + r * THREADS;
+      scale_pre[r] = idx < TN ? s_chan[min(n0 + idx, N - 1)] : s_tok[min(m0 + idx - TN, M - 1)];
+    }
+  }
 
   auto compute = [&](const int8_t* bufp) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      v4i a[4], bb[4];
+      v4i a[FN], bb[FM];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < FN; ++i)
         a[i] = *reinterpret_cast<const v4i*>(bufp + wbase + i * 32 * BK + foff[ks]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < FM; ++j)
         bb[j] = *reinterpret_cast<const v4i*>(bufp + xbase + j * 32 * BK + foff[ks]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < FN; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < FM; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], bb[j], acc[i][j], 0, 0, 0);
     }
   };
@@ -489,7 +524,7 @@ __global__ __launch_bounds__(pf::THREADS, 1) void gemm_prefill_kernel(
   {                                                                  \
     const int st = s0 + (J);                                         \
     if (st < nfull) {                                                \
-      if (st + NS - 2 < nfull) W8A8_WAIT_VM((NS - 2) * DMA_PER_STAGE); \
+      if (st + NS - 2 < nfull) W8A8_WAIT_VM((NS - 2) * DPS);         \
       else W8A8_WAIT_VM(0);                                          \
       barrier_no_fence();                                            \
       if (st + NS - 1 < nfull) issue(st + NS - 1, NEXT);             \
@@ -510,9 +545,9 @@ __global__ __launch_bounds__(pf::THREADS, 1) void gemm_prefill_kernel(
     int8_t* tb = (nfull % NS == 0) ? buf0 : (nfull % NS == 1) ? buf1 : (nfull % NS == 2) ? buf2 : buf3;
     const int64_t k0 = (int64_t)nfull * BK;
     const v4i zero = {0, 0, 0, 0};
-    v4i wv[DMA_PER_OPERAND], xv[DMA_PER_OPERAND];
+    v4i wv[DPO], xv[DPO];
 #pragma unroll
-    for (int i = 0; i < DMA_PER_OPERAND; ++i) {
+    for (int i = 0; i < DPO; ++i) {
       const int p = i * THREADS + wave * kWave + lane;
       const int cidx = (p & 3) ^ lds_swz(p >> 2);
       const bool in = k0 + cidx * 16 < K;
@@ -522,7 +557,7 @@ __global__ __launch_bounds__(pf::THREADS, 1) void gemm_prefill_kernel(
     W8A8_WAIT_VM(0);
     barrier_no_fence();       // every wave is done reading the buffer about to be refilled
 #pragma unroll
-    for (int i = 0; i < DMA_PER_OPERAND; ++i) {
+    for (int i = 0; i < DPO; ++i) {
       *reinterpret_cast<v4i*>(tb + (i * THREADS + wave * kWave + lane) * 16) = wv[i];
       *reinterpret_cast<v4i*>(tb + TILE_BYTES + (i * THREADS + wave * kWave + lane) * 16) = xv[i];
     }
@@ -532,24 +567,280 @@ __global__ __launch_bounds__(pf::THREADS, 1) void gemm_prefill_kernel(
 
   // ---- epilogue: lane holds token m = .. + l % 32 and, per group of 4
   // registers, four consecutive output channels ----
+  float* scale_lds = reinterpret_cast<float*>(buf0);   // [TN channel scales | TM token scales]
+  if constexpr (!I32OUT) {
+    __syncthreads();                                   // all waves are done with buf0
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int m = m0 + wm * 128 + j * 32 + (lane & 31);
+    for (int r = 0; r < kScalesPerThread; ++r) scale_lds[tid + r * THREADS] = scale_pre[r];
+    __syncthreads();
+  }
+#pragma unroll
+  for (int j = 0; j < FM; ++j) {
+    const int ml = wm * FM * 32 + j * 32 + (lane & 31);
+    const int m = m0 + ml;
     if (m >= M) continue;
-    const float st = I32OUT ? 0.0f : s_tok[m];
+    const float st = I32OUT ? 0.0f : scale_lds[TN + ml];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < FN; ++i)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int n = n0 + wn * 128 + i * 32 + 8 * q + 4 * (lane >> 5);
+        const int nl = wn * FN * 32 + i * 32 + 8 * q + 4 * (lane >> 5);
+        const int n = n0 + nl;
         if (n < N) {
           float sc[4] = {0, 0, 0, 0};
-          if constexpr (!I32OUT) load_chan4(s_chan, n, N, sc);
+          if constexpr (!I32OUT) {
+            const float4 v = *reinterpret_cast<const float4*>(scale_lds + nl);
+            sc[0] = v.x; sc[1] = v.y; sc[2] = v.z; sc[3] = v.w;
+          }
           store4<I32OUT>(y, ldy, c, ldc, m, n, N, vec_out, st, sc, acc[i][j][4 * q],
                          acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
         }
       }
   }
+}
+
+// Output tile of workgroup t_lin: tiles are dealt round-robin to the 8 XCDs,
+// so each XCD first gets a run of consecutive tiles (shared W and X panels in
+// its L2), then tiles go in groups of GROUP_M along M.
+__device__ __forceinline__ void prefill_tile_coords(int t_lin, int tiles_n, int tiles_m, int tn,
+                                                    int tm, int& n0, int& m0) {
+  const int T = tiles_n * tiles_m;
+  const int Tq = T / 8;
+  const int t = (t_lin < 8 * Tq) ? (t_lin % 8) * Tq + t_lin / 8 : t_lin;
+  const int group = t / (pf::GROUP_M * tiles_n);
+  const int first_m = group * pf::GROUP_M;
+  const int gsize = min(tiles_m - first_m, pf::GROUP_M);
+  const int in_group = t % (pf::GROUP_M * tiles_n);
+  m0 = (first_m + in_group % gsize) * tm;
+  n0 = (in_group / gsize) * tn;
+}
+
+// ---------------------------------------------------------------------------
+// Prefill kernel, full-line variant (K % 128 == 0): each stage carries 128
+// bytes of K per row, so every DMA request covers whole 128-byte lines
+// (measured on MI355X: 91 GB/s per CU against 54 GB/s for 64-byte
+// half-lines). Two stages: the DMA of stage s + 1 is issued right after the
+// barrier of stage s and lands while stage s is multiplied. Fragment reads
+// are double-buffered in registers: k-step ks + 1's LDS reads are issued
+// before k-step ks's MFMAs.
+//
+// The tile is TNV weight rows (256, or 192 when that packs the CUs better)
+// by 256 token rows; 8 waves in a 2 x 4 grid.
+//
+// LDS row = 128 B = 8 chunks; row r's chunk c sits at slot
+// c ^ swz8(r), swz8(r) = (r & 7) ^ ((r >> 3) & 1): the 8 rows one 8-lane
+// group reads, and the 8 even / 8 odd rows of a 16-lane group, all land in
+// distinct banks. swz8 depends on the low 4 row bits only, so it is the same
+// for every 32-row fragment.
+// ---------------------------------------------------------------------------
+
+namespace pf128 {
+constexpr int TM = 256, BK = 128, WN = 2, WM = 4, THREADS = WN * WM * kWave;
+}  // namespace pf128
+
+__device__ __forceinline__ int lds_swz8(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
+template <int TNV>
+struct Prefill128Cfg {
+  static constexpr int kTN = TNV;
+  static constexpr int kWBytes = TNV * pf128::BK, kXBytes = pf128::TM * pf128::BK;
+  static constexpr int kStageBytes = kWBytes + kXBytes;
+  static constexpr int kFN = TNV / pf128::WN / 32, kFM = pf128::TM / pf128::WM / 32;
+  static constexpr int kDmaW = kWBytes / (pf128::THREADS * 16);
+  static constexpr int kDmaX = kXBytes / (pf128::THREADS * 16);
+  static constexpr int kScales = TNV + pf128::TM;
+  static_assert(kDmaW * pf128::THREADS * 16 == kWBytes && kFN * pf128::WN * 32 == TNV, "");
+};
+
+template <int TNV, bool I32OUT>
+__global__ __launch_bounds__(pf128::THREADS, 1) void gemm_prefill128_kernel(
+    const int8_t* __restrict__ xq, int64_t ldq, const float* __restrict__ s_tok,
+    const int8_t* __restrict__ wq, int64_t ldw, const float* __restrict__ s_chan, int M, int N,
+    int K, uint16_t* __restrict__ y, int64_t ldy, int32_t* __restrict__ c, int64_t ldc,
+    bool vec_out) {
+  using namespace pf128;
+  using C = Prefill128Cfg<TNV>;
+  constexpr int FN = C::kFN, FM = C::kFM, DW = C::kDmaW, DX = C::kDmaX;
+  constexpr int SB = C::kStageBytes, WB = C::kWBytes;
+  __shared__ __attribute__((aligned(1024))) int8_t stages[2 * SB];
+  __shared__ __attribute__((aligned(16))) float scale_lds[C::kScales];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int wn = wave % WN, wm = wave / WN;
+  const int tiles_n = (N + TNV - 1) / TNV, tiles_m = (M + TM - 1) / TM;
+  int n0, m0;
+  prefill_tile_coords(blockIdx.x, tiles_n, tiles_m, TNV, TM, n0, m0);
+
+  // DMA: instruction i of this wave fills LDS chunks [i*THREADS + wave*64, +64)
+  // of an operand tile; chunk p holds row p / 8, global chunk (p % 8) ^ swz8.
+  const int8_t* wsrc[DW];
+  const int8_t* xsrc[DX];
+#pragma unroll
+  for (int i = 0; i < DW; ++i) {
+    const int p = i * THREADS + tid;
+    wsrc[i] = wq + (int64_t)min(n0 + (p >> 3), N - 1) * ldw + ((p & 7) ^ lds_swz8(p >> 3)) * 16;
+  }
+#pragma unroll
+  for (int i = 0; i < DX; ++i) {
+    const int p = i * THREADS + tid;
+    xsrc[i] = xq + (int64_t)min(m0 + (p >> 3), M - 1) * ldq + ((p & 7) ^ lds_swz8(p >> 3)) * 16;
+  }
+  const uint32_t lds_base = lds_addr(stages) + wave * kWave * 16;
+  auto issue = [&](int stage) {
+    const uint32_t base = lds_base + (uint32_t)((stage & 1) * SB);
+    const int64_t k0 = (int64_t)stage * BK;
+#pragma unroll
+    for (int i = 0; i < DW; ++i) dma16(wsrc[i] + k0, base + i * THREADS * 16);
+#pragma unroll
+    for (int i = 0; i < DX; ++i) dma16(xsrc[i] + k0, base + WB + i * THREADS * 16);
+  };
+
+  // scales for the epilogue, fetched before the K loop
+  constexpr int kScalesPerThread = (C::kScales + THREADS - 1) / THREADS;
+  float scale_pre[kScalesPerThread];
+  if constexpr (!I32OUT) {
+#pragma unroll
+    for (int r = 0; r < kScalesPerThread; ++r) {
+      const int idx = tid + r * THREADS;
+      scale_pre[r] = idx < TNV ? s_chan[min(n0 + idx, N - 1)]
+                               : s_tok[min(m0 + min(idx - TNV, TM - 1), M - 1)];
+    }
+  }
+
+  const int frow = lane & 31;
+  const int sw = lds_swz8(frow);
+  int foff[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) foff[ks] = frow * BK + (((2 * ks + (lane >> 5)) ^ sw) << 4);
+  const int wbase = wn * FN * 32 * BK, xbase = WB + wm * FM * 32 * BK;
+
+  v16i acc[FN][FM];
+#pragma unroll
+  for (int i = 0; i < FN; ++i)
+#pragma unroll
+    for (int j = 0; j < FM; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
+
+  v4i fa[2][FN], fb[2][FM];
+  auto read_frags = [&](const int8_t* bufp, int ks, v4i (&a)[FN], v4i (&b)[FM]) {
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+      a[i] = *reinterpret_cast<const v4i*>(bufp + wbase + i * 32 * BK + foff[ks]);
+#pragma unroll
+    for (int j = 0; j < FM; ++j)
+      b[j] = *reinterpret_cast<const v4i*>(bufp + xbase + j * 32 * BK + foff[ks]);
+  };
+
+  const int nst = K / BK;
+  issue(0);
+  for (int s = 0; s < nst; ++s) {
+    W8A8_WAIT_VM(0);                 // this wave's DMA of stage s has landed
+    barrier_no_fence();              // everyone's has; stage s - 1 is fully read
+    if (s + 1 < nst) issue(s + 1);
+    const int8_t* bufp = stages + (s & 1) * SB;
+    read_frags(bufp, 0, fa[0], fb[0]);
+    // The scheduling fences keep each k-step's reads as one block issued
+    // ahead of the previous k-step's MFMAs (left alone, the scheduler
+    // reuses one fragment register and waits on LDS every two MFMAs).
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (ks < 3) read_frags(bufp, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[ks & 1][i], fb[ks & 1][j], acc[i][j],
+                                                            0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // epilogue
+  if constexpr (!I32OUT) {
+#pragma unroll
+    for (int r = 0; r < kScalesPerThread; ++r) {
+      const int idx = tid + r * THREADS;
+      if (idx < C::kScales) scale_lds[idx] = scale_pre[r];
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int j = 0; j < FM; ++j) {
+    const int ml = wm * FM * 32 + j * 32 + (lane & 31);
+    const int m = m0 + ml;
+    if (m >= M) continue;
+    const float st = I32OUT ? 0.0f : scale_lds[TNV + ml];
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int nl = wn * FN * 32 + i * 32 + 8 * q + 4 * (lane >> 5);
+        const int n = n0 + nl;
+        if (n < N) {
+          float sc[4] = {0, 0, 0, 0};
+          if constexpr (!I32OUT) {
+            const float4 v = *reinterpret_cast<const float4*>(scale_lds + nl);
+            sc[0] = v.x; sc[1] = v.y; sc[2] = v.z; sc[3] = v.w;
+          }
+          store4<I32OUT>(y, ldy, c, ldc, m, n, N, vec_out, st, sc, acc[i][j][4 * q],
+                         acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+        }
+      }
+  }
+}
+
+// Compute units of the current device.
+static int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  return cus;
+}
+
+template <int TNV, bool I32OUT>
+static void launch_prefill128(const int8_t* xq, int64_t ldq, const float* s_tok, const int8_t* wq,
+                              int64_t ldw, const float* s_chan, int M, int N, int K, uint16_t* y,
+                              int64_t ldy, int32_t* c, int64_t ldc, bool vec_out, hipStream_t s) {
+  const int tiles = ((N + TNV - 1) / TNV) * ((M + pf128::TM - 1) / pf128::TM);
+  hipLaunchKernelGGL((gemm_prefill128_kernel<TNV, I32OUT>), dim3((unsigned)tiles),
+                     dim3(pf128::THREADS), 0, s, xq, ldq, s_tok, wq, ldw, s_chan, M, N, K, y, ldy,
+                     c, ldc, vec_out);
+}
+
+// 256-row tiles unless 192-row tiles (three quarters of the work each) fill
+// the chip in fewer rounds for this shape.
+template <bool I32OUT>
+static void launch_prefill128_auto(const int8_t* xq, int64_t ldq, const float* s_tok,
+                                   const int8_t* wq, int64_t ldw, const float* s_chan, int M,
+                                   int N, int K, uint16_t* y, int64_t ldy, int32_t* c, int64_t ldc,
+                                   bool vec_out, hipStream_t s) {
+  const int cus = device_cus();
+  const int tm = (M + pf128::TM - 1) / pf128::TM;
+  const int64_t rounds256 = ((int64_t)((N + 255) / 256) * tm + cus - 1) / cus;
+  const int64_t rounds192 = ((int64_t)((N + 191) / 192) * tm + cus - 1) / cus;
+  if (3 * rounds192 < 4 * rounds256)
+    launch_prefill128<192, I32OUT>(xq, ldq, s_tok, wq, ldw, s_chan, M, N, K, y, ldy, c, ldc,
+                                   vec_out, s);
+  else
+    launch_prefill128<256, I32OUT>(xq, ldq, s_tok, wq, ldw, s_chan, M, N, K, y, ldy, c, ldc,
+                                   vec_out, s);
+}
+
+template <int WN, int WM, bool I32OUT>
+static void launch_prefill(const int8_t* xq, int64_t ldq, const float* s_tok, const int8_t* wq,
+                           int64_t ldw, const float* s_chan, int M, int N, int K, uint16_t* y,
+                           int64_t ldy, int32_t* c, int64_t ldc, bool vec_out, hipStream_t s) {
+  const int tiles = ((N + pf::TN - 1) / pf::TN) * ((M + pf::TM - 1) / pf::TM);
+  hipLaunchKernelGGL((gemm_prefill_kernel<WN, WM, I32OUT>), dim3((unsigned)tiles),
+                     dim3(PrefillCfg<WN, WM>::kThreads), 0, s, xq, ldq, s_tok, wq, ldw, s_chan, M,
+                     N, K, y, ldy, c, ldc, vec_out);
 }
 
 // ---------------------------------------------------------------------------
@@ -605,10 +896,12 @@ static hipError_t launch_gemm_t(const int8_t* xq, int64_t ldq, const float* s_to
       else W8A8_SKINNY(4, 1, 8, 8);
     }
 #undef W8A8_SKINNY
+  } else if (M >= kPrefillMinM && K % pf128::BK == 0) {
+    launch_prefill128_auto<I32OUT>(xq, ldq, s_tok, wq, ldw, s_chan, M, N, K, y, ldy, c, ldc,
+                                   vec_out, s);
   } else if (M >= kPrefillMinM) {
-    const int tiles = ((N + pf::TN - 1) / pf::TN) * ((M + pf::TM - 1) / pf::TM);
-    hipLaunchKernelGGL((gemm_prefill_kernel<I32OUT>), dim3((unsigned)tiles), dim3(pf::THREADS), 0, s,
-                       xq, ldq, s_tok, wq, ldw, s_chan, M, N, K, y, ldy, c, ldc, vec_out);
+    launch_prefill<2, 4, I32OUT>(xq, ldq, s_tok, wq, ldw, s_chan, M, N, K, y, ldy, c, ldc, vec_out,
+                                 s);
   } else {
     constexpr int TN = 128, TM = 128, BK = 64, WN = 2, WM = 2;
     const dim3 grid((unsigned)((N + TN - 1) / TN), (unsigned)((M + TM - 1) / TM));

@@ -118,6 +118,10 @@ GEMM_SHAPES = [
     # prefill path (M >= 512): 0..3 full 64-byte stages, K tails, ragged M/N
     (512, 256, 48), (512, 256, 64), (513, 257, 128), (600, 300, 192), (700, 520, 208),
     (1024, 768, 14336 + 16), (2048, 1000, 1024),
+    # full-line prefill path (K % 128 == 0): 1, 2 and 3 stages, several tiles, ragged M/N
+    (512, 512, 128), (777, 300, 256), (1100, 600, 384), (1024, 1024, 4096),
+    # enough tiles that 256-row tiles win over 192-row ones
+    (2048, 8192, 256), (2047, 8190, 256),
 ]
 
 
