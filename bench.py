@@ -42,11 +42,38 @@ def parse():
                    help="skip timing the CPU oracle")
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--detail", action="store_true", help="per-shape timings on stderr")
+    p.add_argument("--counters", action="store_true",
+                   help="eager launches for hardware-counter runs (rocprofv3 --pmc); no timing")
     return p.parse_args()
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+# HBM bytes per launch of the two roofline kernels, from two rocprofv3 --pmc
+# passes over `bench.py --counters` (FETCH_SIZE, then WRITE_SIZE, KiB per
+# dispatch), each scaled by the factor that makes the 1 GiB device copy in the
+# same run count exactly its own bytes. "decode": mean over the 16 decode
+# (projection, M) GEMMs; "prefill": mean over the 4 GEMMs at M = 4096. The
+# figures belong to the GEMM source with the recorded SHA-256 only; for any
+# other source the field is null.
+MEASURED_TRAFFIC = {
+    "gemm_sha256": "ada9bb64f3fe1e30d84e37f5cda9bbf4d4becd5457ad24de19be93e9266c9bb3",
+    "decode": 56396954,
+    "prefill": 426101564,
+}
+GEMM_SRC = os.path.join("int8_w8a8_quantized_token_amd", "csrc", "gemm.hip")
+
+
+def measured_traffic(root, which):
+    import hashlib
+    if not MEASURED_TRAFFIC:
+        return None
+    with open(os.path.join(root, GEMM_SRC), "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != MEASURED_TRAFFIC["gemm_sha256"]:
+            return None
+    return MEASURED_TRAFFIC[which]
 
 
 def lin_bytes(M, N, K):
@@ -185,6 +212,31 @@ def run_phase(torch, S, ms, steps, warmup, detail):
     return ms_step, ms_gemm, launches, per
 
 
+def counters(torch, S, ms, layers=4):
+    """Eager launches for hardware-counter passes: every decode GEMM (projection,
+    M) on `layers` distinct weight buffers, every prefill GEMM once per layer on
+    two layers, then three copies of 1 GiB between device buffers (the
+    calibration: each reads and writes exactly 2^30 bytes)."""
+    for M in ms:
+        for proj, _, _ in S.shapes:
+            S.quantize(proj, M)
+    torch.cuda.synchronize()
+    for M in ms:
+        n = layers if M != PREFILL_M else 2
+        for layer in range(n):
+            for proj, N, K in S.shapes:
+                S.gemm(proj, M, layer)
+        torch.cuda.synchronize()
+        log(f"[counters] M={M}: {n} layers x {len(S.shapes)} GEMMs")
+    src = torch.empty(2**30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log("[counters] 3 x 1 GiB device copies")
+
+
 def cpu_baseline(W, WL, sample_ms, min_seconds=10.0):
     """The oracle, timed on this host on one layer of the decode workload."""
     import numpy as np
@@ -244,6 +296,9 @@ def main():
 
     ms_all = DECODE_MS + (() if args.no_prefill else (PREFILL_M,))
     S = Setup(torch, W, WL, ms_all)
+    if args.counters:
+        counters(torch, S, ms_all)
+        return
 
     # decode (headline)
     d_step, d_gemm, d_launch, d_per = run_phase(torch, S, DECODE_MS, args.steps, args.warmup,
@@ -265,7 +320,10 @@ def main():
                    "layers": LAYERS, "ms": list(DECODE_MS),
                    "shapes_NK": {p: [n, k] for p, n, k in S.shapes}},
         "roofline": {"bound": "hbm", "achieved": round(gemm_gbps, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(gemm_gbps / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(gemm_gbps / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(root, "decode"),
+                     "algorithmic_bytes_per_launch": round(d_gbytes / LAYERS / len(DECODE_MS) /
+                                                           len(S.shapes)),
                      "kernel": "gemm_skinny_kernel", "launches_per_step": d_launch,
                      "avg_launch_us": round(d_gemm / d_launch * 1e3, 3)},
     }
@@ -286,7 +344,10 @@ def main():
                        "m": PREFILL_M},
             "roofline": {"bound": "mfma", "achieved": round(gtops, 1), "peak": INT8_PEAK_TOPS,
                          "unit": "TOPS", "frac": round(gtops / INT8_PEAK_TOPS, 4),
-                         "traffic": None, "kernel": "gemm_tiled_kernel",
+                         "traffic": measured_traffic(root, "prefill"),
+                         "algorithmic_bytes_per_launch": round(sum(
+                             gemm_bytes(PREFILL_M, N, K) for _, N, K in S.shapes) / len(S.shapes)),
+                         "kernel": "gemm_prefill128_kernel",
                          "launches_per_step": p_launch,
                          "avg_launch_us": round(p_gemm / p_launch * 1e3, 3)},
         }
