@@ -96,7 +96,7 @@ struct SkinnyCfg {
   static_assert(NW * RW * MT <= 64, "LDS reduction buffer at most 64 KB");
 };
 
-template <int MT, int RW, int NW, int U, bool I32OUT>
+template <int MT, int RW, int NW, int U, bool I32OUT, bool LATE = false>
 __global__ __launch_bounds__(NW * kWave) void gemm_skinny_kernel(
     const int8_t* __restrict__ xq, int64_t ldq, const float* __restrict__ s_tok,
     const int8_t* __restrict__ wq, int64_t ldw, const float* __restrict__ s_chan, int M, int N,
@@ -118,15 +118,19 @@ __global__ __launch_bounds__(NW * kWave) void gemm_skinny_kernel(
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) xp[mt] = xq + (int64_t)min(mt * 16 + r, M - 1) * ldq + g * 16;
 
-  // Epilogue scales, fetched before the weight stream so that their latency
-  // hides under it.
+  // Epilogue scales: fetched before the weight stream (their latency hides
+  // under it) or, with LATE, after it (they then cost no registers during the
+  // stream and their latency overlaps the LDS reduction).
   float st[MT], sc[RW][4];
-  if constexpr (!I32OUT) {
+  auto load_scales = [&]() {
+    if constexpr (!I32OUT) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) st[mt] = s_tok[min(mt * 16 + r, M - 1)];
+      for (int mt = 0; mt < MT; ++mt) st[mt] = s_tok[min(mt * 16 + r, M - 1)];
 #pragma unroll
-    for (int rw = 0; rw < RW; ++rw) load_chan4(s_chan, n0 + 16 * rw + 4 * g, N, sc[rw]);
-  }
+      for (int rw = 0; rw < RW; ++rw) load_chan4(s_chan, n0 + 16 * rw + 4 * g, N, sc[rw]);
+    }
+  };
+  if constexpr (!LATE) load_scales();
 
   v4i acc[RW][MT];
 #pragma unroll
@@ -183,6 +187,7 @@ __global__ __launch_bounds__(NW * kWave) void gemm_skinny_kernel(
         acc[rw][mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(b[rw], a[mt], acc[rw][mt], 0, 0, 0);
   }
 
+  if constexpr (LATE) load_scales();
 #pragma unroll
   for (int rw = 0; rw < RW; ++rw)
 #pragma unroll
@@ -850,13 +855,13 @@ static void launch_prefill(const int8_t* xq, int64_t ldq, const float* s_tok, co
 constexpr int kSkinnyMaxM = 64;
 constexpr int kPrefillMinM = 512;
 
-template <int MT, int RW, int NW, int U, bool I32OUT>
+template <int MT, int RW, int NW, int U, bool I32OUT, bool LATE = false>
 static void launch_skinny(const int8_t* xq, int64_t ldq, const float* s_tok, const int8_t* wq,
                           int64_t ldw, const float* s_chan, int M, int N, int K, uint16_t* y,
                           int64_t ldy, int32_t* c, int64_t ldc, bool vec_out, hipStream_t s) {
   using C = SkinnyCfg<MT, RW, NW, U>;
   const dim3 grid((unsigned)((N + C::kRows - 1) / C::kRows)), block(C::kThreads);
-  hipLaunchKernelGGL((gemm_skinny_kernel<MT, RW, NW, U, I32OUT>), grid, block, 0, s, xq, ldq,
+  hipLaunchKernelGGL((gemm_skinny_kernel<MT, RW, NW, U, I32OUT, LATE>), grid, block, 0, s, xq, ldq,
                      s_tok, wq, ldw, s_chan, M, N, K, y, ldy, c, ldc, vec_out);
 }
 
@@ -866,34 +871,36 @@ static hipError_t launch_gemm_t(const int8_t* xq, int64_t ldq, const float* s_to
                                 int N, int K, uint16_t* y, int64_t ldy, int32_t* c, int64_t ldc,
                                 bool vec_out, hipStream_t s) {
   if (M <= kSkinnyMaxM) {
-#define W8A8_SKINNY(MTV, RWV, NWV, UV)                                                       \
-  launch_skinny<MTV, RWV, NWV, UV, I32OUT>(xq, ldq, s_tok, wq, ldw, s_chan, M, N, K, y, ldy, c, \
-                                           ldc, vec_out, s)
+#define W8A8_SKINNY(MTV, RWV, NWV, UV, LATEV)                                            \
+  launch_skinny<MTV, RWV, NWV, UV, I32OUT, LATEV>(xq, ldq, s_tok, wq, ldw, s_chan, M, N, K, y, \
+                                                  ldy, c, ldc, vec_out, s)
     // Shape classes measured on MI355X (Llama-3.1-8B projection shapes). More
     // weight rows per wave (RW) reuse each token fragment more often but
-    // leave fewer workgroups; they pay off once N is large or M > 16.
+    // leave fewer workgroups; they pay off once N is large or M > 16. Late
+    // scale loads (last argument) where the scales held through the weight
+    // stream would cost a wave per SIMD.
     const bool wide = N > 8192, mid = N > 4096 && N <= 8192, deep = K > 8192;
     if (M <= 4) {
-      if (mid) W8A8_SKINNY(1, 2, 8, 8);
-      else W8A8_SKINNY(1, 1, 16, 8);
+      if (mid) W8A8_SKINNY(1, 2, 8, 8, false);
+      else W8A8_SKINNY(1, 1, 16, 8, false);
     } else if (M <= 16) {
-      if (wide) W8A8_SKINNY(1, 4, 8, 2);
-      else if (mid) W8A8_SKINNY(1, 2, 8, 8);
-      else if (deep) W8A8_SKINNY(1, 1, 8, 4);
-      else W8A8_SKINNY(1, 1, 16, 8);
+      if (wide) W8A8_SKINNY(1, 4, 8, 2, false);
+      else if (mid) W8A8_SKINNY(1, 2, 8, 8, true);
+      else if (deep) W8A8_SKINNY(1, 1, 8, 4, false);
+      else W8A8_SKINNY(1, 1, 16, 8, false);
     } else if (M <= 32) {
-      if (wide) W8A8_SKINNY(2, 4, 4, 2);
-      else if (mid) W8A8_SKINNY(2, 2, 8, 4);
-      else W8A8_SKINNY(2, 1, 16, 4);
+      if (wide) W8A8_SKINNY(2, 4, 4, 2, true);
+      else if (mid) W8A8_SKINNY(2, 2, 8, 4, false);
+      else W8A8_SKINNY(2, 1, 16, 4, false);
     } else if (M <= 48) {
-      if (wide) W8A8_SKINNY(3, 4, 4, 2);
-      else if (mid) W8A8_SKINNY(3, 2, 8, 2);
-      else W8A8_SKINNY(3, 1, 16, 2);
+      if (wide) W8A8_SKINNY(3, 4, 4, 2, false);
+      else if (mid) W8A8_SKINNY(3, 2, 8, 2, false);
+      else W8A8_SKINNY(3, 1, 16, 2, false);
     } else {
-      if (wide) W8A8_SKINNY(4, 4, 4, 2);
-      else if (mid) W8A8_SKINNY(4, 2, 8, 2);
-      else if (deep) W8A8_SKINNY(4, 1, 16, 2);
-      else W8A8_SKINNY(4, 1, 8, 8);
+      if (wide) W8A8_SKINNY(4, 4, 4, 2, true);
+      else if (mid) W8A8_SKINNY(4, 2, 8, 2, false);
+      else if (deep) W8A8_SKINNY(4, 1, 16, 2, false);
+      else W8A8_SKINNY(4, 1, 8, 8, false);
     }
 #undef W8A8_SKINNY
   } else if (M >= kPrefillMinM && K % pf128::BK == 0) {

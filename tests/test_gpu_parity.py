@@ -112,6 +112,8 @@ GEMM_SHAPES = [
     # skinny path (M <= 64)
     (1, 1, 16), (1, 16, 64), (4, 17, 48), (16, 100, 80), (17, 256, 192), (33, 300, 1040),
     (48, 64, 4096), (64, 4096, 4096), (5, 6144, 14336 + 16),
+    # skinny classes that load the epilogue scales after the weight stream
+    (12, 6000, 1024), (20, 9000, 256), (64, 8320, 512),
     # tiled path
     (65, 1, 16), (65, 128, 64), (100, 129, 112), (128, 256, 4096), (130, 300, 1040),
     (257, 515, 208), (512, 512, 2048), (1000, 384, 4096 + 48),
