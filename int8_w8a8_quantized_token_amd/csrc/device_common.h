@@ -31,6 +31,31 @@ __device__ __forceinline__ int int8_code(float v) {
   return (int)r;
 }
 
+// ---------------------------------------------------------------------------
+// Division-free form of the quantizer's code step. Where it applies it
+// returns what the division gives (IEEE binary32, round to nearest even,
+// denormals kept); elsewhere the callers divide.
+// tests/exhaustive/quantize_fastpath_check.c checks it on the host.
+// ---------------------------------------------------------------------------
+
+// Codes: the int8 code of v / S (round half away from zero, clamp) from
+// t = RN(v R), R = RN(1 / S), S in [2^-100, 2^100]. t lies within
+// 3 * 2^-24 * |v / S| + 2^-148 of RN(v / S), which is below 2^-15 while
+// |v / S| <= 128.0001. So when n = rint(t) satisfies |t - n| < 1/2 - 2^-15,
+// the quotient lies strictly within 1/2 of n and rounds to n under any tie
+// rule; |t| >= 128 means a clamped code. ok is false for the rest (about 6
+// values in 10^5), which divide.
+constexpr float kTieGuard = 0x1p-15f;
+
+__device__ __forceinline__ bool code_fast_ok(float S) { return S >= 0x1p-100f && S <= 0x1p100f; }
+
+__device__ __forceinline__ float code_fast(float v, float R, bool& ok) {
+  const float t = v * R;
+  const float n = __builtin_rintf(t);
+  ok = fabsf(t - n) < 0.5f - kTieGuard || fabsf(t) >= 128.0f;
+  return fminf(fmaxf(n, -kQMax), kQMax);
+}
+
 __device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
   return (uint32_t)(a & 0xFF) | ((uint32_t)(b & 0xFF) << 8) |
          ((uint32_t)(c & 0xFF) << 16) | ((uint32_t)(d & 0xFF) << 24);

@@ -27,6 +27,7 @@
 namespace w8a8 {
 
 constexpr int kRowThreads = 256;      // threads per row, large M
+constexpr int kRowThreadsLongK = 512; // threads per row, large M and K > 8192
 constexpr int kRowThreadsSmallM = 1024; // threads per row when few rows fill the chip
 constexpr int64_t kSmallM = 512;
 
@@ -54,11 +55,29 @@ __device__ __forceinline__ void load_prep8(const uint16_t* __restrict__ xr,
   }
 }
 
+// Codes of 8 values under one row scale, stored as 8 bytes. R = RN(1 / scale)
+// and fast = code_fast_ok(scale); values the fast form leaves open (and all
+// of them when fast is false) are divided. A scale of 0 gives code 0.
 __device__ __forceinline__ void store_codes8(int8_t* __restrict__ qr, int vi, const float (&v)[8],
-                                             float scale) {
+                                             float scale, float R, bool fast) {
   int c[8];
+  if (scale == 0.0f) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) c[e] = (scale == 0.0f) ? 0 : int8_code(v[e] / scale);
+    for (int e = 0; e < 8; ++e) c[e] = 0;
+  } else {
+    uint32_t slow = fast ? 0u : 0xFFu;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      bool ok;
+      c[e] = (int)code_fast(v[e], R, ok);
+      slow |= ok ? 0u : (1u << e);
+    }
+    if (slow != 0u) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (slow & (1u << e)) c[e] = int8_code(v[e] / scale);
+    }
+  }
   uint2 packed;
   packed.x = pack4_i8(c[0], c[1], c[2], c[3]);
   packed.y = pack4_i8(c[4], c[5], c[6], c[7]);
@@ -107,10 +126,12 @@ __global__ __launch_bounds__(BS) void quantize_rows_kernel(
     amax = block_max<BS>(amax, red);
     const float S = amax / kQMax;
     if (tid == 0) scale[row] = S;
+    const bool fast = code_fast_ok(S);
+    const float R = fast ? 1.0f / S : 0.0f;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int vi = tid + i * BS;
-      if (vi < nvec) store_codes8(qr, vi, v[i], S);
+      if (vi < nvec) store_codes8(qr, vi, v[i], S, R, fast);
     }
   } else {
     float amax = 0.0f;
@@ -123,10 +144,12 @@ __global__ __launch_bounds__(BS) void quantize_rows_kernel(
     amax = block_max<BS>(amax, red);
     const float S = amax / kQMax;
     if (tid == 0) scale[row] = S;
+    const bool fast = code_fast_ok(S);
+    const float R = fast ? 1.0f / S : 0.0f;
     for (int vi = tid; vi < nvec; vi += BS) {
       float v[8];
       load_prep8<MODE, SMOOTH>(xr, smooth, vi, v);
-      store_codes8(qr, vi, v, S);
+      store_codes8(qr, vi, v, S, R, fast);
     }
   }
 }
@@ -166,6 +189,8 @@ static hipError_t launch_rows_nv(const uint16_t* x, int64_t ldx, const float* sm
                                  hipStream_t s) {
   if (rows <= kSmallM)
     return launch_rows_bs<kRowThreadsSmallM, MODE, SMOOTH>(x, ldx, smooth, rows, K, q, ldq, scale, s);
+  if (K > 8192)
+    return launch_rows_bs<kRowThreadsLongK, MODE, SMOOTH>(x, ldx, smooth, rows, K, q, ldq, scale, s);
   return launch_rows_bs<kRowThreads, MODE, SMOOTH>(x, ldx, smooth, rows, K, q, ldq, scale, s);
 }
 

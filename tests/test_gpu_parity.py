@@ -36,7 +36,11 @@ def i8(shape, *key):
 # ---------------------------------------------------------------------------
 
 QA_SHAPES = [(1, 16), (2, 48), (3, 64), (15, 4096 + 16), (16, 4096), (17, 2048),
-             (63, 512), (64, 14336), (65, 4096), (127, 1040), (255, 256), (4, 40960)]
+             (63, 512), (64, 14336), (65, 4096), (127, 1040), (255, 256), (4, 40960),
+             # many rows: several rows per workgroup, ragged M and channel tails,
+             # and K beyond the register-resident limit
+             (513, 4096), (1024, 4096 + 16), (1100, 14336), (2049, 2048), (8200, 64),
+             (600, 40960)]
 
 
 @pytest.mark.parametrize("M,K", QA_SHAPES, ids=[f"M{m}_K{k}" for m, k in QA_SHAPES])
@@ -85,6 +89,42 @@ def test_quantize_act_crafted_rows(K):
     np.testing.assert_array_equal(host(xq), xq_ref)
     # the tie rows really hit the tie rule
     assert host(xq)[2, :16].tolist()[:11] == [127, 63, -63, 1, -1, 2, -2, 127, -127, 3, -3]
+
+
+@pytest.mark.parametrize("K", [64, 4096])
+def test_quantize_act_crafted_rows_many(K):
+    # the same edge rows, 60 times over: past 512 rows the many-row kernel runs
+    x32 = np.tile(crafted_rows(K), (60, 1))
+    x = O.round_to_bf16(x32)
+    xq_ref, s_ref = O.quantize_act(x)
+    xq, s = W.w8a8_quantize_act(dev_bf16(x))
+    torch().cuda.synchronize()
+    np.testing.assert_array_equal(host(s).view(np.uint32), s_ref.view(np.uint32))
+    np.testing.assert_array_equal(host(xq), xq_ref)
+
+
+@pytest.mark.parametrize("M", [16, 600])
+def test_quantize_act_smoothing_edges(M):
+    # smoothing factors outside [2^-20, 2^20] and activations below 2^-80 or
+    # exactly zero take the division; the rest the reciprocal form
+    K = 1024
+    r = WL.rng("smooth-edges", M, K)
+    smooth = np.exp(r.uniform(-3, 3, K)).astype(F32)
+    smooth[::17] = F32(2.0 ** -30)
+    smooth[5::17] = F32(2.0 ** 30)
+    smooth[9::17] = F32(2.0 ** -20)
+    smooth[11::17] = F32(2.0 ** 20)
+    x32 = O.bf16_to_f32(act(M, K, "smooth-edges"))
+    x32[:, ::13] = F32(2.0 ** -100)
+    x32[:, 3::13] = F32(-(2.0 ** -81))
+    x32[:, 7::13] = F32(0.0)
+    x32[1, :] = F32(2.0 ** -90)                  # a row of tiny values only
+    x = O.round_to_bf16(x32)
+    xq_ref, s_ref = O.quantize_act(x, smooth)
+    xq, s = W.w8a8_quantize_act(dev_bf16(x), dev(smooth))
+    torch().cuda.synchronize()
+    np.testing.assert_array_equal(host(s).view(np.uint32), s_ref.view(np.uint32))
+    np.testing.assert_array_equal(host(xq), xq_ref)
 
 
 def test_quantize_act_strided_and_empty():
