@@ -283,3 +283,141 @@ def linear(x_bf16: np.ndarray, smooth, wq: np.ndarray, s_chan: np.ndarray):
     acc = gemm_i32(xq, wq)
     y64, y = dequant_epilogue(acc, s_tok, s_chan)
     return {"xq": xq, "s_tok": s_tok, "acc": acc, "y64": y64, "y": y}
+
+
+# ---------------------------------------------------------------------------
+# static per-tensor activation scale, calibrated offline ([PTQ])
+# ---------------------------------------------------------------------------
+#
+# [PTQ] "The Heart of PTQ: Entropy-Based Calibration" fixes one scale per
+# activation tensor ahead of time instead of one per token at run time:
+# min-max calibration maps the largest magnitude seen to 127; entropy
+# calibration clips at the threshold T that loses the least information
+# (smallest KL divergence between the clipped histogram and its quantized
+# version) and uses S = T / 127. The run-time step then needs no reduction,
+# and the clamp to [-127, 127] binds for values beyond the threshold.
+#
+# Readings where the page leaves the procedure open (it is partly garbled):
+#   * magnitudes |x'| are histogrammed (the int8 grid is symmetric), in
+#     HIST_BINS equal bins over [0, amax]: bin = floor(|x'| / w) with
+#     w = amax / HIST_BINS, both binary32 divisions, clamped to the last bin;
+#   * candidate thresholds are bin edges T_i = i * w, i = QUANT_LEVELS ..
+#     HIST_BINS (the page moves T inward from the maximum);
+#   * reference distribution P_i: bins 0 .. i-1 of the histogram h, the mass
+#     beyond T_i folded into bin i-1 (saturated values land on the top code);
+#   * quantized distribution Q_i: the values inside [0, T_i) only, i.e. h[0..i)
+#     split into QUANT_LEVELS groups [g*i // L, (g+1)*i // L) (the 128 code
+#     magnitudes 0..127), each group's count spread evenly over its bins
+#     with h > 0;
+#   * KL(P_i || Q_i) = sum over p > 0 of p log(p / q), P_i and Q_i each
+#     normalized to sum 1, in binary64; a bin with p > 0 and q = 0 makes the
+#     candidate infinitely bad; the smallest i with the minimal value wins;
+#   * T = i * w and S = T / 127 in binary32.
+
+HIST_BINS = 2048
+QUANT_LEVELS = 128
+
+
+def minmax_calibration(act_absmax: np.ndarray, smooth=None):
+    """amax = max_j |x'[., j]| and S = amax / 127 from per-channel maxima.
+
+    [PTQ] "1. Min-Max Calibration". ``act_absmax[j]`` = max over calibration
+    tokens of |x[m, j]| (bf16 values, as act_channel_absmax returns). Since
+    RN(a / s) is monotone in a for s > 0, max_m |RN(x / s)| = RN(max_m|x| / s),
+    so the smoothed maximum is one division per channel. Returns float32
+    (amax, S).
+    """
+    a = np.asarray(act_absmax, dtype=F32)
+    if smooth is not None:
+        a = smooth_activations(a[None, :], smooth)[0]
+    amax = F32(np.max(a)) if a.size else F32(0)
+    return amax, F32(amax / F32(QMAX))
+
+
+def abs_histogram(x_bf16: np.ndarray, smooth, amax, bins: int = HIST_BINS) -> np.ndarray:
+    """Counts of |x'| in ``bins`` equal bins over [0, amax] (int64 [bins]).
+
+    bin = floor(RN(|x'| / w)), w = RN(amax / bins), clamped to bins - 1;
+    amax == 0 puts every value in bin 0.
+    """
+    xs = smooth_activations(bf16_to_f32(x_bf16), smooth)
+    a = np.abs(xs).ravel()
+    amax = F32(amax)
+    if amax == 0:
+        idx = np.zeros(a.shape, np.int64)
+    else:
+        w = F32(amax / F32(bins))
+        idx = np.floor(a / w).astype(np.int64)
+        idx = np.clip(idx, 0, bins - 1)
+    return np.bincount(idx, minlength=bins).astype(np.int64)
+
+
+def entropy_kl(hist: np.ndarray, levels: int = QUANT_LEVELS) -> np.ndarray:
+    """KL(P_i || Q_i) for every candidate i (float64 [bins + 1], NaN below
+    ``levels``, +inf where Q_i misses mass of P_i), following the readings
+    above. An empty histogram gives 0 everywhere."""
+    h = np.asarray(hist, dtype=np.float64)
+    bins = h.size
+    kl = np.full(bins + 1, np.nan)
+    if h.sum() == 0:
+        kl[levels:] = 0.0
+        return kl
+    for i in range(levels, bins + 1):
+        p = h[:i].copy()
+        p[i - 1] += h[i:].sum()                      # saturated mass
+        q = np.zeros(i)
+        for g in range(levels):
+            lo, hi = g * i // levels, (g + 1) * i // levels
+            seg = h[lo:hi]
+            used = seg > 0
+            if used.any():
+                q[lo:hi][used] = seg.sum() / used.sum()
+        if q.sum() == 0:                             # nothing below T_i
+            kl[i] = np.inf
+            continue
+        pn, qn = p / p.sum(), q / q.sum()
+        m = pn > 0
+        if np.any(qn[m] == 0):
+            kl[i] = np.inf
+            continue
+        kl[i] = float(np.sum(pn[m] * np.log(pn[m] / qn[m])))
+    return kl
+
+
+def entropy_calibration(hist: np.ndarray, amax, levels: int = QUANT_LEVELS):
+    """The KL-minimizing threshold. Returns (i, T, S, kl) with T = i * w and
+    S = T / 127 in binary32 (w = amax / bins). [PTQ] "2. Entropy Calibration:
+    Minimizing Information Loss"."""
+    kl = entropy_kl(hist, levels)
+    bins = len(hist)
+    i_best = levels + int(np.argmin(kl[levels:]))   # first minimum
+    w = F32(F32(amax) / F32(bins))
+    T = F32(F32(i_best) * w)
+    return i_best, T, F32(T / F32(QMAX)), kl
+
+
+def quantize_act_static_f32(x32: np.ndarray, smooth, scale):
+    """q = clamp(round(x' / S), -127, 127) with one fixed scale S for every
+    token; returns (q int8 [M, K], S repeated as float32 [M]). S == 0 gives
+    zero codes. [PTQ] "1. Min-Max Calibration" (S = T / 127, symmetric
+    range); [HALF] "How SmoothQuant prevents outliers in activation tensors"
+    (a fixed scale: its codes at S = 0.012 saturate at 127)."""
+    x32 = np.asarray(x32, dtype=F32)
+    assert x32.ndim == 2 and np.all(np.isfinite(x32)), "finite [M, K] input"
+    xs = smooth_activations(x32, smooth)
+    S = F32(scale)
+    s_tok = np.full(x32.shape[0], S, dtype=F32)
+    return quantize_with_scale(xs, s_tok[:, None]), s_tok
+
+
+def quantize_act_static(x_bf16: np.ndarray, smooth, scale):
+    """quantize_act_static_f32 on bf16 activations given as uint16 bit patterns."""
+    return quantize_act_static_f32(bf16_to_f32(x_bf16), smooth, scale)
+
+
+def linear_static(x_bf16: np.ndarray, smooth, scale, wq: np.ndarray, s_chan: np.ndarray):
+    """Steps 1-5 with a static activation scale. Returns every intermediate."""
+    xq, s_tok = quantize_act_static(x_bf16, smooth, scale)
+    acc = gemm_i32(xq, wq)
+    y64, y = dequant_epilogue(acc, s_tok, s_chan)
+    return {"xq": xq, "s_tok": s_tok, "acc": acc, "y64": y64, "y": y}

@@ -95,6 +95,50 @@ def _quantize_weight_per_input(w32):
     return O.quantize_with_scale(w32, sw[None, :]), sw
 
 
+def _entropy_variant(fold=True, q_from_p=False, spread_all=False):
+    def kl_fn(hist, levels=O.QUANT_LEVELS):
+        h = np.asarray(hist, dtype=np.float64)
+        bins = h.size
+        kl = np.full(bins + 1, np.nan)
+        for i in range(levels, bins + 1):
+            p = h[:i].copy()
+            if fold:
+                p[i - 1] += h[i:].sum()
+            src = p if q_from_p else h[:i]
+            q = np.zeros(i)
+            for g in range(levels):
+                lo, hi = g * i // levels, (g + 1) * i // levels
+                seg = src[lo:hi]
+                used = np.ones_like(seg, bool) if spread_all else seg > 0
+                if used.any():
+                    q[lo:hi][used] = seg.sum() / used.sum()
+            pn, qn = p / p.sum(), q / max(q.sum(), 1e-300)
+            m = pn > 0
+            kl[i] = np.inf if np.any(qn[m] == 0) else float(np.sum(pn[m] * np.log(pn[m] / qn[m])))
+        return kl
+    return kl_fn
+
+
+def _histogram_rounds(x_bf16, smooth, amax, bins=O.HIST_BINS):   # nearest bin, not floor
+    xs = O.smooth_activations(O.bf16_to_f32(x_bf16), smooth)
+    a = np.abs(xs).ravel()
+    if F32(amax) == 0:
+        return np.bincount(np.zeros(a.shape, np.int64), minlength=bins)
+    w = F32(F32(amax) / F32(bins))
+    idx = np.clip(np.rint(a / w).astype(np.int64), 0, bins - 1)
+    return np.bincount(idx, minlength=bins)
+
+
+def _minmax_no_smoothing(act_absmax, smooth=None):
+    a = np.asarray(act_absmax, dtype=F32)
+    amax = F32(np.max(a))
+    return amax, F32(amax / F32(127))
+
+
+def _static_uses_token_scale(x32, smooth, scale):
+    return O.quantize_act_f32(x32, smooth)
+
+
 MUTANTS = {
     "ties_to_even": ("round_half_away", _rint_round),
     "ties_toward_plus_inf": ("round_half_away", _ceil_ties),
@@ -111,6 +155,12 @@ MUTANTS = {
     "smoothing_inverted": ("smoothing_factors", _smoothing_inverted),
     "smooth_weight_divides": ("smooth_weight", _smooth_weight_div),
     "weight_scale_per_input_channel": ("quantize_weight_f32", _quantize_weight_per_input),
+    "entropy_no_saturation_fold": ("entropy_kl", _entropy_variant(fold=False)),
+    "entropy_q_from_clipped_p": ("entropy_kl", _entropy_variant(q_from_p=True)),
+    "entropy_spread_over_empty_bins": ("entropy_kl", _entropy_variant(spread_all=True)),
+    "histogram_nearest_bin": ("abs_histogram", _histogram_rounds),
+    "minmax_ignores_smoothing": ("minmax_calibration", _minmax_no_smoothing),
+    "static_uses_token_scale": ("quantize_act_static_f32", _static_uses_token_scale),
 }
 
 PINS = [getattr(P, n) for n in dir(P)

@@ -414,3 +414,166 @@ def test_w8a8_output_close_to_unquantized_and_smoothing_helps():
     e_plain, e_smooth = rel(None), rel(s)
     assert e_smooth < 0.05
     assert e_smooth < e_plain
+
+
+# ---------------------------------------------------------------------------
+# static per-tensor scale: calibration ([PTQ]) and fixed-scale quantization
+# ---------------------------------------------------------------------------
+
+def test_minmax_calibration_closed_form():
+    # [PTQ] "1. Min-Max Calibration": S = max(|min|, |max|) / 127
+    x = np.array([[-3.0, 1.0, 0.5], [2.0, -0.5, -2.5]], dtype=F32)
+    amax, S = O.minmax_calibration(O.act_channel_absmax(O.round_to_bf16(x)))
+    assert Fraction(float(amax)) == 3 and Fraction(float(S)) == rn32(Fraction(3, 127))
+    # with smoothing the maxima of x / s count: 3/2, 1/4, 2.5/0.5 = 5
+    s = np.array([2.0, 4.0, 0.5], dtype=F32)
+    amax, S = O.minmax_calibration(O.act_channel_absmax(O.round_to_bf16(x)), s)
+    assert Fraction(float(amax)) == 5 and Fraction(float(S)) == rn32(Fraction(5, 127))
+
+
+def test_minmax_from_channel_maxima_equals_tensor_maximum():
+    # max over tokens of RN(x / s) equals RN(max|x| / s): the per-channel route
+    # gives the same amax as scanning every smoothed element exactly
+    r = np.random.default_rng(11)
+    x = O.round_to_bf16(r.standard_normal((40, 24)).astype(F32) * F32(3))
+    s = np.exp(r.uniform(-2, 2, 24)).astype(F32)
+    amax, _ = O.minmax_calibration(O.act_channel_absmax(x), s)
+    xf = O.bf16_to_f32(x)
+    want = max(abs(rn32(Fraction(float(v)) / Fraction(float(s[j]))))
+               for row in xf for j, v in enumerate(row))
+    assert Fraction(float(amax)) == want
+
+
+def test_histogram_vs_exact_bins():
+    # bin = floor(RN(|x'| / w)), w = RN(amax / bins), clamped; checked with
+    # exact rationals, including values on bin edges and beyond amax
+    r = np.random.default_rng(12)
+    bins = 64
+    x = O.round_to_bf16(r.standard_normal((6, 16)).astype(F32))
+    xf = O.bf16_to_f32(x)
+    xf[0, :4] = [0.0, -0.0, 0.25, -0.75]               # edges when w = 1/64 * amax
+    s = np.exp(r.uniform(-1, 1, 16)).astype(F32)
+    s[:4] = 1.0
+    x = O.round_to_bf16(xf)
+    amax = F32(2.0)                                      # some |x'| lie beyond it
+    h = O.abs_histogram(x, s, amax, bins)
+    w = rn32(Fraction(2) / bins)
+    want = [0] * bins
+    for row in O.bf16_to_f32(x):
+        for j, v in enumerate(row):
+            xs = rn32(Fraction(float(v)) / Fraction(float(s[j])))
+            b = math.floor(rn32(abs(xs) / w))
+            want[min(b, bins - 1)] += 1
+    assert h.tolist() == want
+    assert h[0] >= 2 and h[8] >= 1 and h[24] >= 1       # 0, 0.25 and 0.75 on their edges
+    assert O.abs_histogram(x, None, F32(0.0), bins).tolist() == [x.size] + [0] * (bins - 1)
+
+
+def test_entropy_hand_example():
+    # four bins, two levels, h = [2, 1, 0, 1]:
+    #   i = 2: P = [2, 2]/4, Q = [2, 1]/3          -> KL = 1/2 ln(9/8)
+    #   i = 3: P = [2, 1, 1]/4, Q = [2, 1, 0]/3    -> P has mass where Q has none
+    #   i = 4: P = [2, 1, 0, 1]/4, Q = [1.5, 1.5, 0, 1]/4
+    #          -> KL = 1/2 ln(4/3) + 1/4 ln(2/3)
+    hist = np.array([2, 1, 0, 1])
+    kl = O.entropy_kl(hist, levels=2)
+    assert math.isclose(kl[2], 0.5 * math.log(9 / 8), rel_tol=1e-12)
+    assert math.isinf(kl[3])
+    assert math.isclose(kl[4], 0.5 * math.log(4 / 3) + 0.25 * math.log(2 / 3), rel_tol=1e-12)
+    i, T, S, _ = O.entropy_calibration(hist, F32(1.0), levels=2)
+    assert i == 4 and T == F32(1.0) and Fraction(float(S)) == rn32(Fraction(1, 127))
+
+
+def test_entropy_no_mass_beyond_first_levels():
+    # all values below 128 bins: the first candidate keeps every bin as its own
+    # code and clips nothing, so it loses nothing
+    r = np.random.default_rng(13)
+    bins = 512                                  # any bin count >= 128 behaves alike
+    hist = np.zeros(bins, np.int64)
+    hist[:128] = r.integers(1, 1000, 128)
+    i, T, S, kl = O.entropy_calibration(hist, F32(16.0))
+    assert i == 128 and kl[128] == 0.0
+    assert T == F32(128 * 16.0 / bins)
+
+
+def test_entropy_uniform_keeps_full_range():
+    # a flat histogram is represented exactly by 128 flat groups at the full
+    # range, while any clipping piles mass on one bin
+    bins = 512
+    hist = np.full(bins, 7, np.int64)
+    i, T, S, kl = O.entropy_calibration(hist, F32(3.0))
+    assert i == bins and kl[bins] == 0.0 and T == F32(3.0)
+    assert np.all(kl[128:bins] > 0)
+
+
+def test_entropy_clips_rare_outliers():
+    # [PTQ] "2. Entropy Calibration": the threshold ignores rare outliers.
+    # A normal bulk plus 0.01% of values near 25 sigma: T ends well below
+    # the maximum but above the bulk's 99.9th percentile.
+    r = np.random.default_rng(14)
+    bulk = np.abs(r.standard_normal(200000))
+    out = np.abs(r.normal(25.0, 1.0, 20))
+    vals = np.concatenate([bulk, out])
+    amax = F32(vals.max())
+    bins = 1024
+    w = float(amax) / bins
+    hist = np.bincount(np.minimum((vals / w).astype(np.int64), bins - 1), minlength=bins)
+    i, T, S, kl = O.entropy_calibration(hist, amax)
+    assert np.quantile(bulk, 0.999) < float(T) < 0.5 * float(amax)
+
+
+def test_quantize_act_static_page_example():
+    # [HALF] "How SmoothQuant prevents outliers in activation tensors": at the
+    # page's fixed scale 0.012 the smoothed activation quantizes to the printed
+    # codes, with the exact ties 62.5 and 127.5 going to 63 and 127
+    g = golden("half_smoothquant_gamma.json")
+    act = np.array(g["activation_printed"], dtype=F32)
+    q, s_tok = O.quantize_act_static_f32(act[None, :], np.array(g["smooth"], dtype=F32),
+                                         F32(g["scale_printed"]))
+    assert q[0].tolist() == g["q_printed_at_scale_printed"]
+    assert s_tok.tolist() == [F32(g["scale_printed"])]
+
+
+def test_quantize_act_static_clamp_binds_and_brute_force():
+    r = np.random.default_rng(15)
+    S = F32(0.0317)
+    x = r.standard_normal((5, 32)).astype(F32) * F32(2)
+    x[0, :6] = [200 * S, -200 * S, 127.4 * S, 127.6 * S, -1e6, 1e6]   # beyond the range
+    s = np.exp(r.uniform(-1, 1, 32)).astype(F32)
+    s[:6] = 1.0
+    q, s_tok = O.quantize_act_static_f32(x, s, S)
+    assert np.all(s_tok == S)
+    assert q[0, :6].tolist() == [127, -127, 127, 127, -127, 127]
+    for m in range(5):
+        for j in range(32):
+            xs = rn32(Fraction(float(x[m, j])) / Fraction(float(s[j])))
+            want = max(-127, min(127, half_away(rn32(xs / Fraction(float(S))))))
+            assert q[m, j] == want
+    assert np.all(O.quantize_act_static_f32(x, s, F32(0))[0] == 0)
+
+
+def test_static_reduces_to_dynamic_for_one_token():
+    # with one token and S equal to its own per-token scale, the static and
+    # the dynamic quantizers coincide
+    r = np.random.default_rng(16)
+    x = O.round_to_bf16(r.standard_normal((1, 300)).astype(F32) * F32(4))
+    s = np.exp(r.uniform(-1, 1, 300)).astype(F32)
+    q_dyn, S_dyn = O.quantize_act(x, s)
+    q_st, S_st = O.quantize_act_static(x, s, S_dyn[0])
+    assert np.array_equal(q_dyn, q_st) and np.array_equal(S_dyn, S_st)
+
+
+def test_linear_static_composition():
+    r = np.random.default_rng(17)
+    x = O.round_to_bf16(r.standard_normal((3, 64)).astype(F32))
+    wq = r.integers(-127, 128, (5, 64)).astype(np.int8)
+    sw = np.exp(r.uniform(-6, -3, 5)).astype(F32)
+    S = F32(0.021)
+    out = O.linear_static(x, None, S, wq, sw)
+    q, _ = O.quantize_act_static(x, None, S)
+    for m in range(3):
+        for n in range(5):
+            acc = sum(int(q[m, k]) * int(wq[n, k]) for k in range(64))
+            assert out["acc"][m, n] == acc
+            y = rnbf16(Fraction(acc) * Fraction(float(S)) * Fraction(float(sw[n])))
+            assert int(out["y"][m, n]) == bf16_bits_of(y)
