@@ -93,7 +93,7 @@ class Setup:
         self.shapes = wl.shapes
         self.ms = ms
         dev = "cuda"
-        self.s, self.sw, self.wq = {}, {}, {}
+        self.s, self.sw, self.wq, self.S_static = {}, {}, {}, {}
         self.x, self.y, self.ws, self.xq, self.st = {}, {}, {}, {}, {}
         t0 = time.time()
         for proj, N, K in self.shapes:
@@ -108,6 +108,10 @@ class Setup:
             wq, sw = W.w8a8_quantize_weight(w_d, s)
             del w_d
             self.s[proj], self.sw[proj] = s, sw
+            # static per-tensor activation scale, entropy-calibrated on the GPU
+            amax, _ = W.w8a8_calibrate_minmax(W.w8a8_channel_absmax(xcal_d), s)
+            hist = W.w8a8_activation_histogram(xcal_d, s, amax)
+            self.S_static[proj], _ = W.w8a8_calibrate_entropy(hist, amax)
             # layer 0 owns the prepared weight; layers 1.. get copies in
             # distinct buffers so every layer streams its own bytes from HBM
             self.wq[proj] = [wq] + [wq.clone() for _ in range(LAYERS - 1)]
@@ -135,6 +139,11 @@ class Setup:
         W = self.W
         W.w8a8_linear(self.x[proj, M], self.s[proj], self.wq[proj][layer], self.sw[proj],
                       y=self.y[proj, M], workspace=self.ws[proj, M])
+
+    def linear_static(self, proj, M, layer):
+        self.W.w8a8_linear_static(self.x[proj, M], self.s[proj], self.S_static[proj],
+                                  self.wq[proj][layer], self.sw[proj], y=self.y[proj, M],
+                                  workspace=self.ws[proj, M])
 
     def quantize(self, proj, M):
         self.W.w8a8_quantize_act(self.x[proj, M], self.s[proj], xq=self.xq[proj, M],
@@ -329,6 +338,22 @@ def main():
     }
     if d_per:
         out["per_shape_decode"] = d_per
+
+    # the same decode step with the static (calibrated, per-tensor) activation scale
+    def static_step():
+        for M in DECODE_MS:
+            for layer in range(LAYERS):
+                for proj, _, _ in S.shapes:
+                    S.linear_static(proj, M, layer)
+    g_static = capture(torch, static_step)
+    s_step = time_graph(torch, g_static, args.steps, args.warmup)
+    del g_static
+    s_value = d_bytes / (s_step * 1e-3) / 1e9
+    log(f"[bench] static-scale decode step {s_step:.3f} ms -> {s_value:.0f} GB/s")
+    out["static_decode"] = {
+        "value": round(s_value, 1), "unit": "GB/s", "ms_per_step": round(s_step, 4),
+        "config": {"workload": "llama8b_decode as above, w8a8_linear_static with one "
+                               "entropy-calibrated activation scale per projection"}}
 
     if not args.no_prefill:
         p_step, p_gemm, p_launch, p_per = run_phase(torch, S, (PREFILL_M,), max(args.steps // 4, 3),

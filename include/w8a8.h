@@ -181,6 +181,84 @@ w8a8_status_t w8a8_quantize_weight(const uint16_t* w, int64_t ldw, const float* 
                                    int64_t N, int64_t K, int8_t* wq, int64_t ldwq,
                                    float* s_chan, hipStream_t stream);
 
+/* ----------------------------------------------------------------------- *
+ * Static per-tensor activation scale. The article "INT8 Post-Training
+ * Quantization for LLM Inference on NVIDIA GPUs", section "The Heart of PTQ:
+ * Entropy-Based Calibration", fixes one activation scale per tensor ahead of
+ * time (min-max or entropy calibration) instead of one per token at run
+ * time. The run-time step then needs no reduction and the clamp binds for
+ * values beyond the calibrated threshold.
+ * ----------------------------------------------------------------------- */
+
+#define W8A8_HIST_BINS 2048    /* default histogram size for entropy calibration */
+#define W8A8_QUANT_LEVELS 128  /* code magnitudes 0..127; smallest candidate threshold */
+
+/*
+ * Quantization with one fixed scale S = scale[0] for every token:
+ *   x'[m,k] = x[m,k] / smooth[k] (binary32 division; skipped when NULL)
+ *   xq[m,k] = clamp(round(x'[m,k] / S), -127, 127), round half away from 0
+ *   s_tok[m] = S for every row (so that w8a8_gemm applies it)
+ * S == 0 gives all-zero codes. Cited: "1. Min-Max Calibration" (S = T / 127,
+ * symmetric range) in the calibration section above.
+ *   x [M, K] bf16, ldx >= K; smooth [K] or NULL; scale [1] fp32, finite,
+ *   >= 0 (device memory, read)
+ *   xq [M, K] int8, ldq >= K; s_tok [M] fp32 (written)
+ */
+w8a8_status_t w8a8_quantize_act_static(const uint16_t* x, int64_t ldx, const float* smooth,
+                                       const float* scale, int64_t M, int64_t K, int8_t* xq,
+                                       int64_t ldq, float* s_tok, hipStream_t stream);
+
+/*
+ * w8a8_linear with the static scale: w8a8_quantize_act_static into the
+ * workspace (same layout and size as w8a8_linear's), then w8a8_gemm.
+ */
+w8a8_status_t w8a8_linear_static(const uint16_t* x, int64_t ldx, const float* smooth,
+                                 const float* scale, const int8_t* wq, int64_t ldw,
+                                 const float* s_chan, int64_t M, int64_t N, int64_t K,
+                                 uint16_t* y, int64_t ldy, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Min-max calibration ("1. Min-Max Calibration"):
+ *   amax[0]  = max_k act_absmax[k] / smooth[k]   (binary32 division; the
+ *              largest |x'| seen, since rounding is monotone)
+ *   scale[0] = amax[0] / 127
+ *   act_absmax [K] fp32 from w8a8_channel_absmax over the calibration
+ *   tokens; smooth [K] or NULL (read). amax, scale [1] fp32 (written). K > 0.
+ */
+w8a8_status_t w8a8_calibrate_minmax(const float* act_absmax, const float* smooth, int64_t K,
+                                    float* amax, float* scale, hipStream_t stream);
+
+/*
+ * Histogram of |x'| for entropy calibration ("2. Entropy Calibration"):
+ *   w = amax[0] / bins; bin = floor(min(|x'| / w, bins - 1)) (binary32;
+ *   values at or past amax land in the last bin; w == 0 puts all in bin 0)
+ *   hist[bin] += 1, accumulated across calls (zero it before the first batch).
+ *   x [rows, K] bf16, ldx >= K, K % 8 == 0; smooth [K] or NULL; amax [1] fp32
+ *   (e.g. from w8a8_calibrate_minmax) (read). hist [bins] uint32 (read and
+ *   written). 128 <= bins <= 8192. Counts wrap past 2^32 - 1 per bin.
+ */
+w8a8_status_t w8a8_activation_histogram(const uint16_t* x, int64_t ldx, const float* smooth,
+                                        int64_t rows, int64_t K, const float* amax, int64_t bins,
+                                        uint32_t* hist, hipStream_t stream);
+
+/*
+ * Entropy calibration ("2. Entropy Calibration: Minimizing Information
+ * Loss"): for every candidate threshold T_i = i * w, i = 128 .. bins,
+ *   P_i = hist[0..i) with the counts past T_i added to bin i-1 (saturation),
+ *   Q_i = hist[0..i) merged into 128 groups [g*i/128, (g+1)*i/128) and each
+ *         group's count spread evenly over its nonzero bins,
+ *   KL_i = sum over P_i > 0 of p log(p / q) (each normalized; binary64;
+ *          +inf where Q_i is 0 under mass of P_i);
+ * the smallest i with the least KL gives scale[0] = (i * w) / 127
+ * (binary32, w = amax[0] / bins).
+ *   hist [bins] uint32, amax [1] fp32 (read); scale [1] fp32 (written);
+ *   kl [bins + 1] fp64 or NULL (written: KL_i at index i, NaN below 128).
+ *   128 <= bins <= 8192. One workgroup: an offline step, not a hot one.
+ */
+w8a8_status_t w8a8_calibrate_entropy(const uint32_t* hist, int64_t bins, const float* amax,
+                                     float* scale, double* kl, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -40,7 +40,16 @@ _SIGNATURES = {
     "w8a8_channel_absmax": (_i, [_p, _i64, _i64, _i64, _p, _p]),
     "w8a8_smoothing_factors": (_i, [_p, _p, _i64, _p, _p]),
     "w8a8_quantize_weight": (_i, [_p, _i64, _p, _i64, _i64, _p, _i64, _p, _p]),
+    "w8a8_quantize_act_static": (_i, [_p, _i64, _p, _p, _i64, _i64, _p, _i64, _p, _p]),
+    "w8a8_linear_static": (_i, [_p, _i64, _p, _p, _p, _i64, _p, _i64, _i64, _i64, _p, _i64,
+                                _p, _sz, _p]),
+    "w8a8_calibrate_minmax": (_i, [_p, _p, _i64, _p, _p, _p]),
+    "w8a8_activation_histogram": (_i, [_p, _i64, _p, _i64, _i64, _p, _i64, _p, _p]),
+    "w8a8_calibrate_entropy": (_i, [_p, _i64, _p, _p, _p, _p]),
 }
+
+HIST_BINS = 2048       # W8A8_HIST_BINS
+QUANT_LEVELS = 128     # W8A8_QUANT_LEVELS
 
 _LIB = None
 
@@ -235,3 +244,89 @@ def w8a8_quantize_weight(w, smooth=None, wq=None, s_chan=None, stream=None):
                                       _vec(s_chan, "s_chan"), _stream(stream)),
            "w8a8_quantize_weight")
     return wq, s_chan
+
+
+# ---------------------------------------------------------------------------
+# static per-tensor activation scale
+# ---------------------------------------------------------------------------
+
+def w8a8_quantize_act_static(x, smooth, scale, xq=None, s_tok=None, stream=None):
+    """x bf16 [M, K], scale fp32 [1] (device) -> (xq int8 [M, K], s_tok fp32 [M] = scale)."""
+    torch = _torch()
+    M, K = x.shape
+    if xq is None:
+        xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    if s_tok is None:
+        s_tok = torch.empty((M,), dtype=torch.float32, device=x.device)
+    px, ldx = _mat(x, _bf16_types(), "x")
+    pq, ldq = _mat(xq, (torch.int8,), "xq")
+    _check(lib().w8a8_quantize_act_static(px, ldx, _vec(smooth, "smooth"), _vec(scale, "scale"),
+                                          M, K, pq, ldq, _vec(s_tok, "s_tok"), _stream(stream)),
+           "w8a8_quantize_act_static")
+    return xq, s_tok
+
+
+def w8a8_linear_static(x, smooth, scale, wq, s_chan, y=None, workspace=None, stream=None):
+    """x bf16 [M, K] -> y bf16 [M, N] with the fixed activation scale scale[0]."""
+    torch = _torch()
+    M, K = x.shape
+    N = wq.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    nbytes = w8a8_linear_workspace_bytes(M, K)
+    if workspace is None:
+        workspace = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=x.device)
+    px, ldx = _mat(x, _bf16_types(), "x")
+    pw, ldw = _mat(wq, (torch.int8,), "wq")
+    py, ldy = _mat(y, _bf16_types(), "y")
+    _check(lib().w8a8_linear_static(px, ldx, _vec(smooth, "smooth"), _vec(scale, "scale"), pw, ldw,
+                                    _vec(s_chan, "s_chan"), M, N, K, py, ldy, workspace.data_ptr(),
+                                    workspace.numel() * workspace.element_size(),
+                                    _stream(stream)),
+           "w8a8_linear_static")
+    return y
+
+
+def w8a8_calibrate_minmax(act_absmax, smooth=None, amax=None, scale=None, stream=None):
+    """Per-channel maxima [K] -> (amax fp32 [1], scale fp32 [1]) on the device."""
+    torch = _torch()
+    K = act_absmax.shape[0]
+    dev = act_absmax.device
+    amax = torch.empty((1,), dtype=torch.float32, device=dev) if amax is None else amax
+    scale = torch.empty((1,), dtype=torch.float32, device=dev) if scale is None else scale
+    _check(lib().w8a8_calibrate_minmax(_vec(act_absmax, "act_absmax"), _vec(smooth, "smooth"), K,
+                                       _vec(amax, "amax"), _vec(scale, "scale"), _stream(stream)),
+           "w8a8_calibrate_minmax")
+    return amax, scale
+
+
+def w8a8_activation_histogram(x, smooth, amax, bins=HIST_BINS, hist=None, stream=None):
+    """Adds the |x'| counts of x bf16 [rows, K] to hist (uint32 [bins], kept in
+    an int32 tensor; zero-initialized when not given) and returns it."""
+    torch = _torch()
+    rows, K = x.shape
+    if hist is None:
+        hist = torch.zeros((bins,), dtype=torch.int32, device=x.device)
+    px, ldx = _mat(x, _bf16_types(), "x")
+    _check(lib().w8a8_activation_histogram(px, ldx, _vec(smooth, "smooth"), rows, K,
+                                           _vec(amax, "amax"), bins,
+                                           _vec(hist, "hist", torch.int32), _stream(stream)),
+           "w8a8_activation_histogram")
+    return hist
+
+
+def w8a8_calibrate_entropy(hist, amax, scale=None, kl=None, want_kl=False, stream=None):
+    """hist [bins] (int32 tensor holding uint32 counts), amax [1] -> (scale fp32 [1],
+    kl fp64 [bins + 1] or None)."""
+    torch = _torch()
+    bins = hist.shape[0]
+    dev = hist.device
+    scale = torch.empty((1,), dtype=torch.float32, device=dev) if scale is None else scale
+    if kl is None and want_kl:
+        kl = torch.empty((bins + 1,), dtype=torch.float64, device=dev)
+    _check(lib().w8a8_calibrate_entropy(_vec(hist, "hist", torch.int32), bins, _vec(amax, "amax"),
+                                        _vec(scale, "scale"),
+                                        _vec(kl, "kl", torch.float64) if kl is not None else None,
+                                        _stream(stream)),
+           "w8a8_calibrate_entropy")
+    return scale, kl

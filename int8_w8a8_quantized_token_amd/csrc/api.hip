@@ -10,6 +10,8 @@
 namespace {
 
 constexpr int64_t kMaxK = 131072;  // 128 * 128 * K stays below 2^31
+constexpr int64_t kMinBins = W8A8_QUANT_LEVELS;
+constexpr int64_t kMaxBins = 8192;
 constexpr int64_t kMaxDim = INT32_MAX;
 
 inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -144,6 +146,80 @@ w8a8_status_t w8a8_linear(const uint16_t* x, int64_t ldx, const float* smooth, c
                                                xq, K, s_tok, stream)));
   return from_hip(w8a8::launch_gemm(xq, K, s_tok, wq, ldw, s_chan, M, N, K, y, ldy, nullptr, 0,
                                     stream));
+}
+
+w8a8_status_t w8a8_quantize_act_static(const uint16_t* x, int64_t ldx, const float* smooth,
+                                       const float* scale, int64_t M, int64_t K, int8_t* xq,
+                                       int64_t ldq, float* s_tok, hipStream_t stream) {
+  W8A8_TRY(check_dims(M, K));
+  if (M == 0) return W8A8_SUCCESS;
+  W8A8_TRY(check_matrix(x, ldx, M, K, 2));
+  W8A8_TRY(check_matrix(xq, ldq, M, K, 1));
+  W8A8_TRY(check_vector(scale));
+  W8A8_TRY(check_vector(s_tok));
+  if (smooth) W8A8_TRY(check_vector(smooth));
+  return from_hip(w8a8::launch_quantize_static(x, ldx, smooth, scale, M, K, xq, ldq, s_tok, stream));
+}
+
+w8a8_status_t w8a8_linear_static(const uint16_t* x, int64_t ldx, const float* smooth,
+                                 const float* scale, const int8_t* wq, int64_t ldw,
+                                 const float* s_chan, int64_t M, int64_t N, int64_t K, uint16_t* y,
+                                 int64_t ldy, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream) {
+  W8A8_TRY(check_dims(M, K, N));
+  if (M == 0 || N == 0) return W8A8_SUCCESS;
+  W8A8_TRY(check_matrix(x, ldx, M, K, 2));
+  W8A8_TRY(check_matrix(wq, ldw, N, K, 1));
+  W8A8_TRY(check_vector(scale));
+  W8A8_TRY(check_vector(s_chan));
+  if (smooth) W8A8_TRY(check_vector(smooth));
+  W8A8_TRY(check_out_matrix(y, ldy, M, N, 2));
+  if (workspace == nullptr || workspace_bytes < w8a8_linear_workspace_bytes(M, K))
+    return W8A8_ERROR_WORKSPACE;
+  if (!aligned(workspace, 256)) return W8A8_ERROR_MISALIGNED;
+
+  int8_t* xq = static_cast<int8_t*>(workspace);
+  float* s_tok = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256((size_t)M * K));
+  W8A8_TRY(from_hip(
+      w8a8::launch_quantize_static(x, ldx, smooth, scale, M, K, xq, K, s_tok, stream)));
+  return from_hip(w8a8::launch_gemm(xq, K, s_tok, wq, ldw, s_chan, M, N, K, y, ldy, nullptr, 0,
+                                    stream));
+}
+
+w8a8_status_t w8a8_calibrate_minmax(const float* act_absmax, const float* smooth, int64_t K,
+                                    float* amax, float* scale, hipStream_t stream) {
+  if (K <= 0) return W8A8_ERROR_INVALID_VALUE;
+  if (K > kMaxDim) return W8A8_ERROR_UNSUPPORTED;
+  W8A8_TRY(check_vector(act_absmax));
+  W8A8_TRY(check_vector(amax));
+  W8A8_TRY(check_vector(scale));
+  if (smooth) W8A8_TRY(check_vector(smooth));
+  return from_hip(w8a8::launch_calibrate_minmax(act_absmax, smooth, K, amax, scale, stream));
+}
+
+w8a8_status_t w8a8_activation_histogram(const uint16_t* x, int64_t ldx, const float* smooth,
+                                        int64_t rows, int64_t K, const float* amax, int64_t bins,
+                                        uint32_t* hist, hipStream_t stream) {
+  if (rows < 0 || K <= 0) return W8A8_ERROR_INVALID_VALUE;
+  if (K % 8 != 0 || K > kMaxDim / 8 || rows > kMaxDim || bins < kMinBins || bins > kMaxBins)
+    return W8A8_ERROR_UNSUPPORTED;
+  if (rows == 0) return W8A8_SUCCESS;
+  W8A8_TRY(check_matrix(x, ldx, rows, K, 2));
+  W8A8_TRY(check_vector(amax));
+  W8A8_TRY(check_vector(hist));
+  if (smooth) W8A8_TRY(check_vector(smooth));
+  return from_hip(
+      w8a8::launch_abs_histogram(x, ldx, smooth, rows, K, amax, bins, hist, stream));
+}
+
+w8a8_status_t w8a8_calibrate_entropy(const uint32_t* hist, int64_t bins, const float* amax,
+                                     float* scale, double* kl, hipStream_t stream) {
+  if (bins < kMinBins || bins > kMaxBins) return W8A8_ERROR_UNSUPPORTED;
+  W8A8_TRY(check_vector(hist));
+  W8A8_TRY(check_vector(amax));
+  W8A8_TRY(check_vector(scale));
+  if (kl && !aligned(kl, 8)) return W8A8_ERROR_MISALIGNED;
+  return from_hip(w8a8::launch_calibrate_entropy(hist, bins, amax, scale, kl, stream));
 }
 
 w8a8_status_t w8a8_channel_absmax(const uint16_t* a, int64_t lda, int64_t rows, int64_t K,

@@ -11,6 +11,7 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 
 constexpr int kWave = 64;     // CDNA wavefront width
 constexpr float kQMax = 127.0f;
+constexpr int kQuantLevels = 128;   // code magnitudes 0..127
 
 // bf16 bit pattern -> float (exact).
 __device__ __forceinline__ float bf16_lo(uint32_t two) { return __uint_as_float(two << 16); }

@@ -29,4 +29,19 @@ hipError_t launch_gemm(const int8_t* xq, int64_t ldq, const float* s_tok,
                        uint16_t* y, int64_t ldy, int32_t* acc, int64_t ldc,
                        hipStream_t s);
 
+// Static per-tensor scale: quantizer and calibration (static_scale.hip).
+hipError_t launch_quantize_static(const uint16_t* x, int64_t ldx, const float* smooth,
+                                  const float* scale, int64_t M, int64_t K, int8_t* q,
+                                  int64_t ldq, float* s_tok, hipStream_t s);
+
+hipError_t launch_calibrate_minmax(const float* act_absmax, const float* smooth, int64_t K,
+                                   float* amax, float* scale, hipStream_t s);
+
+hipError_t launch_abs_histogram(const uint16_t* x, int64_t ldx, const float* smooth, int64_t rows,
+                                int64_t K, const float* amax, int64_t bins, uint32_t* hist,
+                                hipStream_t s);
+
+hipError_t launch_calibrate_entropy(const uint32_t* hist, int64_t bins, const float* amax,
+                                    float* scale, double* kl, hipStream_t s);
+
 }  // namespace w8a8

@@ -337,18 +337,19 @@ def minmax_calibration(act_absmax: np.ndarray, smooth=None):
 def abs_histogram(x_bf16: np.ndarray, smooth, amax, bins: int = HIST_BINS) -> np.ndarray:
     """Counts of |x'| in ``bins`` equal bins over [0, amax] (int64 [bins]).
 
-    bin = floor(RN(|x'| / w)), w = RN(amax / bins), clamped to bins - 1;
-    amax == 0 puts every value in bin 0.
+    bin = floor(min(RN(|x'| / w), bins - 1)), w = RN(amax / bins): values at
+    or beyond amax land in the last bin. When w is 0 (amax 0, or so small
+    that amax / bins underflows) every value goes to bin 0.
     """
     xs = smooth_activations(bf16_to_f32(x_bf16), smooth)
     a = np.abs(xs).ravel()
-    amax = F32(amax)
-    if amax == 0:
+    w = F32(F32(amax) / F32(bins))
+    if w == 0:
         idx = np.zeros(a.shape, np.int64)
     else:
-        w = F32(amax / F32(bins))
-        idx = np.floor(a / w).astype(np.int64)
-        idx = np.clip(idx, 0, bins - 1)
+        with np.errstate(over="ignore"):
+            ratio = (a / w).astype(F32)
+        idx = np.floor(np.minimum(ratio, F32(bins - 1))).astype(np.int64)
     return np.bincount(idx, minlength=bins).astype(np.int64)
 
 

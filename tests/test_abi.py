@@ -23,7 +23,7 @@ def lib():
 
 def test_exports_every_header_function(lib):
     names = W.header_functions()
-    assert len(names) == 10
+    assert len(names) == 15
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
@@ -121,6 +121,36 @@ def test_prep_validation(lib):
     assert qw(A, 4096, None, 16, 4096, A, 4096, None, None) == INVALID
     assert qw(A, 4096, None, 16, 4104, A, 4104, A, None) == UNSUPPORTED
     assert qw(A, 4096, None, 0, 4096, None, 4096, None, None) == OK
+
+
+def test_static_scale_validation(lib):
+    qs = lib.w8a8_quantize_act_static
+    assert qs(A, 4096, None, None, 16, 4096, A, 4096, A, None) == INVALID       # no scale
+    assert qs(A, 4096, None, A + 2, 16, 4096, A, 4096, A, None) == MISALIGNED
+    assert qs(A, 4096, None, A, 16, 24, A, 24, A, None) == UNSUPPORTED         # K % 16
+    assert qs(MIS, 4096, None, A, 16, 4096, A, 4096, A, None) == MISALIGNED
+    assert qs(None, 4096, None, None, 0, 4096, None, 4096, None, None) == OK   # empty
+    ls = lib.w8a8_linear_static
+    assert ls(A, 4096, None, A, A, 4096, A, 16, 4096, 4096, A, 4096, None, 0, None) == WORKSPACE
+    assert ls(A, 4096, None, None, A, 4096, A, 16, 4096, 4096, A, 4096, A, 1 << 30, None) == INVALID
+    assert ls(None, 4096, None, None, None, 4096, None, 0, 4096, 4096, None, 4096, None, 0,
+              None) == OK
+    cm = lib.w8a8_calibrate_minmax
+    assert cm(A, None, 0, A, A, None) == INVALID
+    assert cm(None, None, 16, A, A, None) == INVALID
+    assert cm(A, None, 16, A, A + 1, None) == MISALIGNED
+    ah = lib.w8a8_activation_histogram
+    assert ah(A, 4096, None, 16, 4096, A, 127, A, None) == UNSUPPORTED          # bins
+    assert ah(A, 4096, None, 16, 4096, A, 8193, A, None) == UNSUPPORTED
+    assert ah(A, 12, None, 16, 12, A, 2048, A, None) == UNSUPPORTED             # K % 8
+    assert ah(A, 4096, None, 16, 4096, None, 2048, A, None) == INVALID          # no amax
+    assert ah(A, 4096, None, 16, 4096, A, 2048, None, None) == INVALID          # no hist
+    assert ah(None, 4096, None, 0, 4096, None, 2048, None, None) == OK          # no rows
+    ce = lib.w8a8_calibrate_entropy
+    assert ce(A, 100, A, A, None, None) == UNSUPPORTED
+    assert ce(None, 2048, A, A, None, None) == INVALID
+    assert ce(A, 2048, A, None, None, None) == INVALID
+    assert ce(A, 2048, A, A, A + 4, None) == MISALIGNED                         # kl alignment
 
 
 def test_python_binding_raises_typed_error(lib):
