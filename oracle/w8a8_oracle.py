@@ -41,8 +41,9 @@ Precision and rounding (the readings taken where the pages leave it open):
   * Step 4 is exact: the float64 matmul below only ever holds integers of
     magnitude <= 128*128*K < 2**53, so every product and partial sum is exact
     whatever order the library uses.
-  * Step 5 is evaluated in binary64 (the value acc*S*sw carries a relative
-    error of at most 2**-53) and rounded once to bf16, round-to-nearest-even.
+  * Step 5 is a binary32 chain, float(acc) * S then * sw, each product
+    rounded, then bf16 round-to-nearest-even (the "fp32, then rounded" value
+    outputs are judged against); a binary64 value is kept for error reports.
   * bf16 values are handled as their uint16 bit patterns.
 
 Parity pins: every function here is checked in tests/test_oracle_pins.py
@@ -264,17 +265,25 @@ def gemm_i32(xq: np.ndarray, wq: np.ndarray) -> np.ndarray:
 
 
 def dequant_epilogue(acc: np.ndarray, s_tok: np.ndarray, s_chan: np.ndarray):
-    """y[m, n] = acc[m, n] * S[m] * sw[n] in binary64, then once to bf16.
+    """y[m, n] = bf16(RN32(RN32(RN32(acc[m, n]) * S[m]) * sw[n])).
 
     The per-token and per-channel scales factor out of the K-sum, so they are
     applied after accumulation ([HALF] "Why activation quantization is hard";
-    [PERF] "Inter-token latency (ITL)": convert back to BF16).
-    Returns (y float64 [M, N], y bf16 bits uint16 [M, N]).
+    [PERF] "Inter-token latency (ITL)": convert back to BF16). The chain is
+    binary32, one rounding per step in the order written (the accumulator
+    converted, times the token scale, times the channel scale), then bf16
+    round-to-nearest-even: the "fp32, then rounded" value the outputs are
+    compared with. Returns (y64 float64 [M, N], y bf16 bits uint16 [M, N]),
+    y64 = acc * S * sw in binary64 for reporting the error of y.
     """
-    y = (np.asarray(acc, dtype=np.float64)
-         * np.asarray(s_tok, dtype=F32).astype(np.float64)[:, None]
-         * np.asarray(s_chan, dtype=F32).astype(np.float64)[None, :])
-    return y, round_to_bf16(y)
+    acc = np.asarray(acc)
+    st = np.asarray(s_tok, dtype=F32)
+    sc = np.asarray(s_chan, dtype=F32)
+    t = acc.astype(F32)                       # int32 -> binary32, nearest even
+    v = (t * st[:, None]) * sc[None, :]       # binary32 products, in this order
+    y64 = (acc.astype(np.float64) * st.astype(np.float64)[:, None]
+           * sc.astype(np.float64)[None, :])
+    return y64, round_to_bf16(v)
 
 
 def linear(x_bf16: np.ndarray, smooth, wq: np.ndarray, s_chan: np.ndarray):

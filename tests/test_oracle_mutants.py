@@ -139,6 +139,12 @@ def _static_uses_token_scale(x32, smooth, scale):
     return O.quantize_act_f32(x32, smooth)
 
 
+def _epilogue_binary64(acc, s_tok, s_chan):
+    y = (np.asarray(acc, dtype=np.float64) * np.asarray(s_tok, F32).astype(np.float64)[:, None]
+         * np.asarray(s_chan, F32).astype(np.float64)[None, :])
+    return y, O.round_to_bf16(y)
+
+
 MUTANTS = {
     "ties_to_even": ("round_half_away", _rint_round),
     "ties_toward_plus_inf": ("round_half_away", _ceil_ties),
@@ -150,6 +156,7 @@ MUTANTS = {
     "gemm_no_transpose": ("gemm_i32", _gemm_no_transpose),
     "gemm_wrong_orientation": ("gemm_i32", _gemm_wrong_operand),
     "epilogue_scales_swapped": ("dequant_epilogue", _epilogue_swapped),
+    "epilogue_binary64": ("dequant_epilogue", _epilogue_binary64),
     "bf16_truncates": ("round_to_bf16", _bf16_truncate),
     "smoothing_alpha_one": ("smoothing_factors", _smoothing_alpha1),
     "smoothing_inverted": ("smoothing_factors", _smoothing_inverted),

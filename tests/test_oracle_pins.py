@@ -283,9 +283,23 @@ def test_epilogue_vs_fraction():
     for m in range(M):
         for n in range(N):
             exact = Fraction(int(acc[m, n])) * Fraction(float(s_tok[m])) * Fraction(float(s_chan[n]))
-            assert int(y[m, n]) == bf16_bits_of(rnbf16(exact))
+            chain = rn32(rn32(rn32(Fraction(int(acc[m, n]))) * Fraction(float(s_tok[m])))
+                         * Fraction(float(s_chan[n])))
+            assert int(y[m, n]) == bf16_bits_of(rnbf16(chain))
             assert abs(Fraction(float(y64[m, n])) - exact) <= abs(exact) * Fraction(1, 2 ** 52)
+            # the chain stays within one bf16 ulp of the exact value's rounding
+            assert abs(int(y[m, n]) - bf16_bits_of(rnbf16(exact))) <= 1
     assert int(y[0, 0]) == 0
+
+
+def test_epilogue_is_a_binary32_chain():
+    # acc = 2^24 + 2^16 + 1 is not a binary32 value: it converts to
+    # 2^24 (1 + 2^-8), exactly halfway between two bf16 values, and rounds to
+    # the even one (2^24); the exact product is just above halfway (2^24 + 2^17)
+    acc = np.array([[2 ** 24 + 2 ** 16 + 1]], dtype=np.int32)
+    y64, y = O.dequant_epilogue(acc, np.ones(1, F32), np.ones(1, F32))
+    assert int(y[0, 0]) == 0x4B80
+    assert bf16_bits_of(rnbf16(Fraction(int(acc[0, 0])))) == 0x4B81
 
 
 def test_epilogue_scale_orientation():
