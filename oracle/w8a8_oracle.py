@@ -431,3 +431,116 @@ def linear_static(x_bf16: np.ndarray, smooth, scale, wq: np.ndarray, s_chan: np.
     acc = gemm_i32(xq, wq)
     y64, y = dequant_epilogue(acc, s_tok, s_chan)
     return {"xq": xq, "s_tok": s_tok, "acc": acc, "y64": y64, "y": y}
+
+
+# ---------------------------------------------------------------------------
+# fused producers: the ops that feed the linears in a Llama block
+# ---------------------------------------------------------------------------
+#
+# [HALF] "How SmoothQuant prevents outliers in activation tensors" places the
+# outliers in the RMSNorm weight gamma, and "How the SmoothQuant smoothing
+# factor is computed" folds the smoothing division into that weight. A
+# producer that ends in the quantizer therefore emits int8 codes and per-token
+# scales directly. Readings where the pages say nothing:
+#   * RMSNorm: ms = mean of h^2 over the row, the exact sum rounded once to
+#     binary32; inv = 1 / sqrt(ms + eps), each step one binary32 rounding
+#     (sum, square root, division); y = (h * inv) * g with g = gamma / s
+#     folded once per channel (binary32); then per-token quantization of y;
+#   * residual add: h = bf16(h + r), the binary32 sum of two bf16 values
+#     rounded to bf16 (it becomes the new residual stream);
+#   * SiLU-gated product: m = bf16((g / (1 + exp(-g))) * u) evaluated in
+#     binary64 from the bf16 gate and up values and rounded once (binary32
+#     exp is not correctly rounded on either side; in binary64 both sides
+#     round to the same bf16 except within 2^-52 of a rounding boundary);
+#     then x' = m / s and per-token quantization.
+
+def fold_gamma(gamma, smooth) -> np.ndarray:
+    """g = gamma / s (binary32): the smoothing division moved into RMSNorm's
+    weight ([HALF] "How the SmoothQuant smoothing factor is computed")."""
+    gamma = np.asarray(gamma, dtype=F32)
+    if smooth is None:
+        return gamma.copy()
+    return (gamma / np.asarray(smooth, dtype=F32)).astype(F32)
+
+
+def residual_add(h_bf16: np.ndarray, r_bf16: np.ndarray) -> np.ndarray:
+    """bf16(h + r): binary32 sum of two bf16 values, rounded to bf16."""
+    return round_to_bf16(bf16_to_f32(h_bf16) + bf16_to_f32(r_bf16))
+
+
+def rms_inverse(h_bf16: np.ndarray, eps) -> np.ndarray:
+    """inv[m] = RN32(1 / RN32(sqrt(RN32(ms[m] + eps)))), ms the mean of squares
+    of the row (exact sum, one rounding to binary32)."""
+    import math
+    h = bf16_to_f32(h_bf16).astype(np.float64)
+    K = h.shape[1]
+    ms = np.array([math.fsum((row * row).tolist()) / K for row in h]).astype(F32)
+    d = (ms + F32(eps)).astype(F32)
+    return (F32(1) / np.sqrt(d).astype(F32)).astype(F32)
+
+
+def rmsnorm_quantize(h_bf16: np.ndarray, residual, g, eps):
+    """RMSNorm with the folded weight g, then per-token quantization.
+
+    With ``residual`` the row first becomes bf16(h + residual). Returns
+    (q int8 [M, K], S float32 [M], h_out bf16 [M, K] (the residual stream)).
+    """
+    h = np.asarray(h_bf16, dtype=np.uint16)
+    if residual is not None:
+        h = residual_add(h, residual)
+    inv = rms_inverse(h, eps)
+    y = (bf16_to_f32(h) * inv[:, None]).astype(F32) * np.asarray(g, dtype=F32)[None, :]
+    q, S = quantize_act_f32(y.astype(F32))
+    return q, S, h
+
+
+def silu_mul(gu_bf16: np.ndarray) -> np.ndarray:
+    """m = bf16(silu(gate) * up) for gu = [gate | up] (bf16 [M, 2I] -> [M, I])."""
+    x = bf16_to_f32(gu_bf16).astype(np.float64)
+    inter = x.shape[1] // 2
+    g, u = x[:, :inter], x[:, inter:2 * inter]
+    with np.errstate(over="ignore"):
+        m = (g / (1.0 + np.exp(-g))) * u
+    return round_to_bf16(m)
+
+
+def silu_mul_quantize(gu_bf16: np.ndarray, smooth):
+    """silu_mul, then the per-token quantizer (x' = m / s). Returns (q, S)."""
+    return quantize_act(silu_mul(gu_bf16), smooth)
+
+
+def chain_forward(x_bf16: np.ndarray, layers, eps=1e-5):
+    """A stack of Llama-shaped blocks built from the W8A8 linears (one row
+    per token; every step is row-local, so any subset of rows can be run on
+    its own). Per layer:
+
+      q, S, h = rmsnorm_quantize(h, pending, g_attn)      pre-attention norm
+      y_qkv   = linear(q, S; qkv)
+      y_o     = linear(quantize_act(y_qkv[:, :K], s_o); o)  attention stand-in:
+                                                             the q slice
+      q, S, h = rmsnorm_quantize(h, y_o, g_mlp)           residual + norm
+      y_gu    = linear(q, S; gate_up)
+      pending = linear(silu_mul_quantize(y_gu, s_down); down)
+
+    and at the end h = residual_add(h, pending). ``layers`` holds per-layer
+    dicts with keys g_attn, g_mlp (folded norm weights), s_o, s_down
+    (smoothing factors) and (wq, sw) pairs qkv, o, gate_up, down.
+    Returns the final residual stream (bf16 [M, K]).
+    """
+    h = np.asarray(x_bf16, dtype=np.uint16)
+    K = h.shape[1]
+    pending = None
+
+    def lin(q, S, w):
+        return dequant_epilogue(gemm_i32(q, w[0]), S, w[1])[1]
+
+    for L in layers:
+        q, S, h = rmsnorm_quantize(h, pending, L["g_attn"], eps)
+        y_qkv = lin(q, S, L["qkv"])
+        q, S = quantize_act(np.ascontiguousarray(y_qkv[:, :K]), L["s_o"])
+        y_o = lin(q, S, L["o"])
+        q, S, h = rmsnorm_quantize(h, y_o, L["g_mlp"], eps)
+        y_gu = lin(q, S, L["gate_up"])
+        q, S = silu_mul_quantize(y_gu, L["s_down"])
+        pending = lin(q, S, L["down"])
+    return residual_add(h, pending) if pending is not None else h

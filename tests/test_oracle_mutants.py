@@ -145,6 +145,41 @@ def _epilogue_binary64(acc, s_tok, s_chan):
     return y, O.round_to_bf16(y)
 
 
+def _rms_sum_not_mean(h_bf16, eps):
+    import math
+    h = O.bf16_to_f32(h_bf16).astype(np.float64)
+    ss = np.array([math.fsum((row * row).tolist()) for row in h]).astype(F32)
+    return (F32(1) / np.sqrt((ss + F32(eps)).astype(F32)).astype(F32)).astype(F32)
+
+
+def _rms_eps_outside(h_bf16, eps):
+    import math
+    h = O.bf16_to_f32(h_bf16).astype(np.float64)
+    ms = np.array([math.fsum((row * row).tolist()) / h.shape[1] for row in h]).astype(F32)
+    return (F32(1) / (np.sqrt(ms).astype(F32) + F32(eps))).astype(F32)
+
+
+def _fold_gamma_multiplies(gamma, smooth):
+    g = np.asarray(gamma, F32)
+    return g.copy() if smooth is None else (g * np.asarray(smooth, F32)).astype(F32)
+
+
+_real_rmsnorm_quantize = O.rmsnorm_quantize
+
+
+def _rmsnorm_drops_residual(h_bf16, residual, g, eps):
+    return _real_rmsnorm_quantize(h_bf16, None, g, eps)
+
+
+def _silu_halves_swapped(gu_bf16):
+    inter = gu_bf16.shape[1] // 2
+    return _real_silu_mul(
+        np.concatenate([gu_bf16[:, inter:], gu_bf16[:, :inter]], axis=1))
+
+
+_real_silu_mul = O.silu_mul
+
+
 MUTANTS = {
     "ties_to_even": ("round_half_away", _rint_round),
     "ties_toward_plus_inf": ("round_half_away", _ceil_ties),
@@ -168,6 +203,11 @@ MUTANTS = {
     "histogram_nearest_bin": ("abs_histogram", _histogram_rounds),
     "minmax_ignores_smoothing": ("minmax_calibration", _minmax_no_smoothing),
     "static_uses_token_scale": ("quantize_act_static_f32", _static_uses_token_scale),
+    "rms_sum_not_mean": ("rms_inverse", _rms_sum_not_mean),
+    "rms_eps_outside_sqrt": ("rms_inverse", _rms_eps_outside),
+    "fold_gamma_multiplies": ("fold_gamma", _fold_gamma_multiplies),
+    "rmsnorm_drops_residual": ("rmsnorm_quantize", _rmsnorm_drops_residual),
+    "silu_halves_swapped": ("silu_mul", _silu_halves_swapped),
 }
 
 PINS = [getattr(P, n) for n in dir(P)

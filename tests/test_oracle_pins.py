@@ -591,3 +591,121 @@ def test_linear_static_composition():
             assert out["acc"][m, n] == acc
             y = rnbf16(Fraction(acc) * Fraction(float(S)) * Fraction(float(sw[n])))
             assert int(out["y"][m, n]) == bf16_bits_of(y)
+
+
+# ---------------------------------------------------------------------------
+# fused producers (RMSNorm + quantize, SiLU-gated product + quantize)
+# ---------------------------------------------------------------------------
+
+def _rms_inv_exact(row, eps):
+    K = len(row)
+    ms = rn32(sum(Fraction(float(v)) ** 2 for v in row) / K)
+    d = rn32(ms + Fraction(float(F32(eps))))
+    return rn32(Fraction(1) / _sqrt_rn32(d))
+
+
+def test_rms_inverse_vs_fraction():
+    r = np.random.default_rng(20)
+    h = O.round_to_bf16(r.standard_normal((4, 96)).astype(F32) * F32(3))
+    h32 = O.bf16_to_f32(h)
+    h32[1, :5] = [1e-30, -2e-38, 400.0, 0.0, -0.0]
+    h = O.round_to_bf16(h32)
+    inv = O.rms_inverse(h, 1e-5)
+    for m, row in enumerate(O.bf16_to_f32(h)):
+        assert Fraction(float(inv[m])) == _rms_inv_exact(row, 1e-5)
+
+
+def test_rmsnorm_quantize_vs_fraction():
+    r = np.random.default_rng(21)
+    K = 48
+    h = O.round_to_bf16(r.standard_normal((3, K)).astype(F32))
+    res = O.round_to_bf16(r.standard_normal((3, K)).astype(F32) * F32(0.3))
+    gamma = np.ones(K, F32)
+    gamma[[3, 17]] = 20.0                       # the page's outlier mechanism
+    s = np.exp(r.uniform(-1, 1, K)).astype(F32)
+    g = O.fold_gamma(gamma, s)
+    for k in range(K):
+        assert Fraction(float(g[k])) == rn32(Fraction(float(gamma[k])) / Fraction(float(s[k])))
+    q, S, h_out = O.rmsnorm_quantize(h, res, g, 1e-5)
+    hf, rf = O.bf16_to_f32(h), O.bf16_to_f32(res)
+    for m in range(3):
+        summed = [rnbf16(rn32(Fraction(float(a)) + Fraction(float(b)))) for a, b in zip(hf[m], rf[m])]
+        assert [bf16_bits_of(v) for v in summed] == h_out[m].tolist()
+        inv = _rms_inv_exact([float(v) for v in summed], 1e-5)
+        y = [rn32(rn32(v * inv) * Fraction(float(g[k]))) for k, v in enumerate(summed)]
+        a = max(abs(v) for v in y)
+        Sm = rn32(a / 127)
+        assert Fraction(float(S[m])) == Sm
+        assert q[m].tolist() == [max(-127, min(127, half_away(rn32(v / Sm)))) for v in y]
+
+
+def test_rmsnorm_is_scale_invariant_without_eps():
+    # RMSNorm(2^k h) = RMSNorm(h) exactly when eps = 0 (every step scales by a power of 2)
+    r = np.random.default_rng(22)
+    h32 = O.bf16_to_f32(O.round_to_bf16(r.standard_normal((5, 256)).astype(F32)))
+    g = np.exp(r.uniform(-1, 1, 256)).astype(F32)
+    q1, S1, _ = O.rmsnorm_quantize(O.round_to_bf16(h32), None, g, 0.0)
+    q2, S2, _ = O.rmsnorm_quantize(O.round_to_bf16(h32 * F32(16)), None, g, 0.0)
+    assert np.array_equal(q1, q2) and np.array_equal(S1, S2)
+    # a row of +-1 has mean square 1: with g = 1 every code is +-127
+    q, S, _ = O.rmsnorm_quantize(O.round_to_bf16(np.sign(h32[:1]) + F32(0) * h32[:1]),
+                                 None, np.ones(256, F32), 0.0)
+    assert np.all(np.abs(q) == 127) and Fraction(float(S[0])) == rn32(Fraction(1, 127))
+
+
+def _silu_mul_exact(g, u):
+    getcontext().prec = 80
+    gd = Decimal(Fraction(float(g)).numerator) / Decimal(Fraction(float(g)).denominator)
+    ud = Decimal(Fraction(float(u)).numerator) / Decimal(Fraction(float(u)).denominator)
+    val = gd / (1 + (-gd).exp()) * ud
+    bits = bf16_bits_of(rnbf16(Fraction(val)))
+    return bits | 0x8000 if (bits == 0 and val.is_signed()) else bits
+
+
+def test_silu_mul_vs_high_precision():
+    r = np.random.default_rng(23)
+    inter = 40
+    gate = r.standard_normal((3, inter)).astype(F32) * F32(4)
+    up = r.standard_normal((3, inter)).astype(F32)
+    gate[0, :4] = [0.0, -200.0, 90.0, 0.5]
+    up[0, :4] = [5.0, 3.0, -2.0, 1.0]
+    gu = O.round_to_bf16(np.concatenate([gate, up], axis=1))
+    m = O.silu_mul(gu)
+    x = O.bf16_to_f32(gu)
+    for i in range(3):
+        for j in range(inter):
+            assert int(m[i, j]) == _silu_mul_exact(x[i, j], x[i, inter + j])
+    assert O.bf16_to_f32(m[0, :2]).tolist() == [0.0, 0.0]           # silu(0) = 0; underflow
+    assert O.bf16_to_f32(m[0, 2:3]).tolist() == [-180.0]             # silu(90) * -2
+    # gate and up are the two halves in that order: a zero gate zeroes the product
+    gu2 = O.round_to_bf16(np.concatenate([np.zeros((1, 8), F32), np.full((1, 8), 7, F32)], 1))
+    assert np.all(O.bf16_to_f32(O.silu_mul(gu2)) == 0)
+
+
+def test_chain_rows_are_independent():
+    # every op in the chain is row-local: running any subset of rows alone
+    # gives those rows of the full run
+    r = np.random.default_rng(24)
+    K, I = 32, 48
+    def lw(n, k):
+        w = O.round_to_bf16(r.standard_normal((n, k)).astype(F32) * F32(0.05))
+        return O.quantize_weight(w)
+    layers = [{"g_attn": np.ones(K, F32), "g_mlp": np.ones(K, F32), "s_o": None, "s_down": None,
+               "qkv": lw(3 * K, K), "o": lw(K, K), "gate_up": lw(2 * I, K), "down": lw(K, I)}
+              for _ in range(2)]
+    x = O.round_to_bf16(r.standard_normal((7, K)).astype(F32))
+    full = O.chain_forward(x, layers)
+    part = O.chain_forward(x[[1, 4, 6]], layers)
+    assert np.array_equal(full[[1, 4, 6]], part)
+    # one layer by hand
+    one = O.chain_forward(x, layers[:1])
+    L = layers[0]
+    q, S, h = O.rmsnorm_quantize(x, None, L["g_attn"], 1e-5)
+    yq = O.dequant_epilogue(O.gemm_i32(q, L["qkv"][0]), S, L["qkv"][1])[1]
+    q, S = O.quantize_act(np.ascontiguousarray(yq[:, :K]), None)
+    yo = O.dequant_epilogue(O.gemm_i32(q, L["o"][0]), S, L["o"][1])[1]
+    q, S, h = O.rmsnorm_quantize(h, yo, L["g_mlp"], 1e-5)
+    yg = O.dequant_epilogue(O.gemm_i32(q, L["gate_up"][0]), S, L["gate_up"][1])[1]
+    q, S = O.silu_mul_quantize(yg, None)
+    yd = O.dequant_epilogue(O.gemm_i32(q, L["down"][0]), S, L["down"][1])[1]
+    assert np.array_equal(one, O.residual_add(h, yd))
