@@ -259,6 +259,54 @@ w8a8_status_t w8a8_activation_histogram(const uint16_t* x, int64_t ldx, const fl
 w8a8_status_t w8a8_calibrate_entropy(const uint32_t* hist, int64_t bins, const float* amax,
                                      float* scale, double* kl, hipStream_t stream);
 
+/* ----------------------------------------------------------------------- *
+ * Fused producers. Part 1, section "How SmoothQuant prevents outliers in
+ * activation tensors", locates the outliers in RMSNorm's weight, and "How
+ * the SmoothQuant smoothing factor is computed" folds the smoothing division
+ * into that weight; the ops that feed a block's linears can therefore end in
+ * the quantizer and emit codes and per-token scales directly, with no bf16
+ * activation written and read back.
+ * ----------------------------------------------------------------------- */
+
+/*
+ * Optional residual add, RMSNorm with a folded weight, per-token quantization:
+ *   if residual: h[m,k] = bf16(h[m,k] + residual[m,k])   (binary32 sum; h written)
+ *   ms[m]  = sum_k h[m,k]^2 / K, the exact sum rounded once to binary32
+ *   inv[m] = 1 / sqrt(ms[m] + eps)                         (binary32 steps)
+ *   y[m,k] = (h[m,k] * inv[m]) * gamma[k]                  (binary32)
+ *   s_tok[m] = max_k |y[m,k]| / 127; xq = clamp(round(y / s_tok), -127, 127)
+ * gamma is the norm weight divided by the next linear's smoothing factor
+ * (w8a8_fold_gamma).
+ *   h [M, K] bf16, ldh >= K (read; written when residual != NULL);
+ *   residual [M, K] bf16 or NULL; gamma [K] fp32; eps >= 0 (read)
+ *   xq [M, K] int8, ldq >= K; s_tok [M] fp32 (written). K <= 65536.
+ */
+w8a8_status_t w8a8_rmsnorm_quantize(uint16_t* h, int64_t ldh, const uint16_t* residual,
+                                    int64_t ldr, const float* gamma, float eps, int64_t M,
+                                    int64_t K, int8_t* xq, int64_t ldq, float* s_tok,
+                                    hipStream_t stream);
+
+/*
+ * SiLU-gated product and per-token quantization of a gate|up row:
+ *   m[m,k]  = bf16((g / (1 + exp(-g))) * u), g = gu[m,k], u = gu[m,I+k],
+ *             evaluated in binary64 and rounded once
+ *   x'[m,k] = m[m,k] / smooth[k] (binary32; skipped when NULL)
+ *   s_tok[m] = max_k |x'[m,k]| / 127; xq = clamp(round(x' / s_tok), -127, 127)
+ *   gu [M, 2I] bf16, ldgu >= 2I (read); smooth [I] or NULL (read)
+ *   xq [M, I] int8, ldq >= I; s_tok [M] fp32 (written). I % 16 == 0, I <= 65536.
+ */
+w8a8_status_t w8a8_silu_mul_quantize(const uint16_t* gu, int64_t ldgu, const float* smooth,
+                                     int64_t M, int64_t I, int8_t* xq, int64_t ldq, float* s_tok,
+                                     hipStream_t stream);
+
+/* g[k] = gamma[k] / smooth[k] (binary32 division; g = gamma when smooth is NULL). */
+w8a8_status_t w8a8_fold_gamma(const float* gamma, const float* smooth, int64_t K, float* g,
+                              hipStream_t stream);
+
+/* h[m,k] = bf16(h[m,k] + r[m,k]) (binary32 sum of bf16 values). K % 8 == 0. */
+w8a8_status_t w8a8_residual_add(uint16_t* h, int64_t ldh, const uint16_t* r, int64_t ldr,
+                                int64_t M, int64_t K, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -16,6 +16,7 @@ from .binding import (  # noqa: F401
     w8a8_calibrate_entropy,
     w8a8_calibrate_minmax,
     w8a8_channel_absmax,
+    w8a8_fold_gamma,
     w8a8_gemm,
     w8a8_gemm_i32,
     w8a8_linear,
@@ -24,6 +25,9 @@ from .binding import (  # noqa: F401
     w8a8_quantize_act,
     w8a8_quantize_act_static,
     w8a8_quantize_weight,
+    w8a8_residual_add,
+    w8a8_rmsnorm_quantize,
+    w8a8_silu_mul_quantize,
     w8a8_smoothing_factors,
     w8a8_status_string,
 )

@@ -46,6 +46,11 @@ _SIGNATURES = {
     "w8a8_calibrate_minmax": (_i, [_p, _p, _i64, _p, _p, _p]),
     "w8a8_activation_histogram": (_i, [_p, _i64, _p, _i64, _i64, _p, _i64, _p, _p]),
     "w8a8_calibrate_entropy": (_i, [_p, _i64, _p, _p, _p, _p]),
+    "w8a8_rmsnorm_quantize": (_i, [_p, _i64, _p, _i64, _p, ctypes.c_float, _i64, _i64, _p, _i64,
+                                   _p, _p]),
+    "w8a8_silu_mul_quantize": (_i, [_p, _i64, _p, _i64, _i64, _p, _i64, _p, _p]),
+    "w8a8_fold_gamma": (_i, [_p, _p, _i64, _p, _p]),
+    "w8a8_residual_add": (_i, [_p, _i64, _p, _i64, _i64, _i64, _p]),
 }
 
 HIST_BINS = 2048       # W8A8_HIST_BINS
@@ -330,3 +335,61 @@ def w8a8_calibrate_entropy(hist, amax, scale=None, kl=None, want_kl=False, strea
                                         _stream(stream)),
            "w8a8_calibrate_entropy")
     return scale, kl
+
+
+# ---------------------------------------------------------------------------
+# fused producers
+# ---------------------------------------------------------------------------
+
+def w8a8_rmsnorm_quantize(h, gamma, eps=1e-5, residual=None, xq=None, s_tok=None, stream=None):
+    """(residual add into h,) RMSNorm with the folded weight, per-token codes.
+    h bf16 [M, K] (updated in place when residual is given) -> (xq, s_tok)."""
+    torch = _torch()
+    M, K = h.shape
+    if xq is None:
+        xq = torch.empty((M, K), dtype=torch.int8, device=h.device)
+    if s_tok is None:
+        s_tok = torch.empty((M,), dtype=torch.float32, device=h.device)
+    ph, ldh = _mat(h, _bf16_types(), "h")
+    pr, ldr = (None, K) if residual is None else _mat(residual, _bf16_types(), "residual")
+    pq, ldq = _mat(xq, (torch.int8,), "xq")
+    _check(lib().w8a8_rmsnorm_quantize(ph, ldh, pr, ldr, _vec(gamma, "gamma"), float(eps), M, K,
+                                       pq, ldq, _vec(s_tok, "s_tok"), _stream(stream)),
+           "w8a8_rmsnorm_quantize")
+    return xq, s_tok
+
+
+def w8a8_silu_mul_quantize(gu, smooth=None, xq=None, s_tok=None, stream=None):
+    """gu bf16 [M, 2I] (gate | up) -> (xq int8 [M, I], s_tok fp32 [M])."""
+    torch = _torch()
+    M, two_i = gu.shape
+    inter = two_i // 2
+    if xq is None:
+        xq = torch.empty((M, inter), dtype=torch.int8, device=gu.device)
+    if s_tok is None:
+        s_tok = torch.empty((M,), dtype=torch.float32, device=gu.device)
+    pg, ldg = _mat(gu, _bf16_types(), "gu")
+    pq, ldq = _mat(xq, (torch.int8,), "xq")
+    _check(lib().w8a8_silu_mul_quantize(pg, ldg, _vec(smooth, "smooth"), M, inter, pq, ldq,
+                                        _vec(s_tok, "s_tok"), _stream(stream)),
+           "w8a8_silu_mul_quantize")
+    return xq, s_tok
+
+
+def w8a8_fold_gamma(gamma, smooth=None, g=None, stream=None):
+    torch = _torch()
+    K = gamma.shape[0]
+    if g is None:
+        g = torch.empty((K,), dtype=torch.float32, device=gamma.device)
+    _check(lib().w8a8_fold_gamma(_vec(gamma, "gamma"), _vec(smooth, "smooth"), K, _vec(g, "g"),
+                                 _stream(stream)), "w8a8_fold_gamma")
+    return g
+
+
+def w8a8_residual_add(h, r, stream=None):
+    """h = bf16(h + r) in place."""
+    M, K = h.shape
+    ph, ldh = _mat(h, _bf16_types(), "h")
+    pr, ldr = _mat(r, _bf16_types(), "r")
+    _check(lib().w8a8_residual_add(ph, ldh, pr, ldr, M, K, _stream(stream)), "w8a8_residual_add")
+    return h

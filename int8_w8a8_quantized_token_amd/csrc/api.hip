@@ -12,6 +12,7 @@ namespace {
 constexpr int64_t kMaxK = 131072;  // 128 * 128 * K stays below 2^31
 constexpr int64_t kMinBins = W8A8_QUANT_LEVELS;
 constexpr int64_t kMaxBins = 8192;
+constexpr int64_t kMaxProducerK = 65536;   // 8 vectors of 8 per thread at 1024 threads
 constexpr int64_t kMaxDim = INT32_MAX;
 
 inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -220,6 +221,57 @@ w8a8_status_t w8a8_calibrate_entropy(const uint32_t* hist, int64_t bins, const f
   W8A8_TRY(check_vector(scale));
   if (kl && !aligned(kl, 8)) return W8A8_ERROR_MISALIGNED;
   return from_hip(w8a8::launch_calibrate_entropy(hist, bins, amax, scale, kl, stream));
+}
+
+w8a8_status_t w8a8_rmsnorm_quantize(uint16_t* h, int64_t ldh, const uint16_t* residual,
+                                    int64_t ldr, const float* gamma, float eps, int64_t M,
+                                    int64_t K, int8_t* xq, int64_t ldq, float* s_tok,
+                                    hipStream_t stream) {
+  W8A8_TRY(check_dims(M, K));
+  if (K > kMaxProducerK) return W8A8_ERROR_UNSUPPORTED;
+  if (!(eps >= 0.0f) || eps > 3.0e38f) return W8A8_ERROR_INVALID_VALUE;
+  if (M == 0) return W8A8_SUCCESS;
+  W8A8_TRY(check_matrix(h, ldh, M, K, 2));
+  if (residual) W8A8_TRY(check_matrix(residual, ldr, M, K, 2));
+  W8A8_TRY(check_vector(gamma));
+  W8A8_TRY(check_matrix(xq, ldq, M, K, 1));
+  W8A8_TRY(check_vector(s_tok));
+  return from_hip(
+      w8a8::launch_rmsnorm_quantize(h, ldh, residual, ldr, gamma, eps, M, K, xq, ldq, s_tok, stream));
+}
+
+w8a8_status_t w8a8_silu_mul_quantize(const uint16_t* gu, int64_t ldgu, const float* smooth,
+                                     int64_t M, int64_t I, int8_t* xq, int64_t ldq, float* s_tok,
+                                     hipStream_t stream) {
+  W8A8_TRY(check_dims(M, I));
+  if (I > kMaxProducerK) return W8A8_ERROR_UNSUPPORTED;
+  if (M == 0) return W8A8_SUCCESS;
+  W8A8_TRY(check_matrix(gu, ldgu, M, 2 * I, 2));
+  if (smooth) W8A8_TRY(check_vector(smooth));
+  W8A8_TRY(check_matrix(xq, ldq, M, I, 1));
+  W8A8_TRY(check_vector(s_tok));
+  return from_hip(w8a8::launch_silu_mul_quantize(gu, ldgu, smooth, M, I, xq, ldq, s_tok, stream));
+}
+
+w8a8_status_t w8a8_fold_gamma(const float* gamma, const float* smooth, int64_t K, float* g,
+                              hipStream_t stream) {
+  if (K < 0) return W8A8_ERROR_INVALID_VALUE;
+  if (K > kMaxDim) return W8A8_ERROR_UNSUPPORTED;
+  if (K == 0) return W8A8_SUCCESS;
+  W8A8_TRY(check_vector(gamma));
+  W8A8_TRY(check_vector(g));
+  if (smooth) W8A8_TRY(check_vector(smooth));
+  return from_hip(w8a8::launch_fold_gamma(gamma, smooth, K, g, stream));
+}
+
+w8a8_status_t w8a8_residual_add(uint16_t* h, int64_t ldh, const uint16_t* r, int64_t ldr,
+                                int64_t M, int64_t K, hipStream_t stream) {
+  if (M < 0 || K <= 0) return W8A8_ERROR_INVALID_VALUE;
+  if (K % 8 != 0 || K > kMaxDim / 8 || M > kMaxDim) return W8A8_ERROR_UNSUPPORTED;
+  if (M == 0) return W8A8_SUCCESS;
+  W8A8_TRY(check_matrix(h, ldh, M, K, 2));
+  W8A8_TRY(check_matrix(r, ldr, M, K, 2));
+  return from_hip(w8a8::launch_residual_add(h, ldh, r, ldr, M, K, stream));
 }
 
 w8a8_status_t w8a8_channel_absmax(const uint16_t* a, int64_t lda, int64_t rows, int64_t K,

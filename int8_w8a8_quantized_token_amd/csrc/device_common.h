@@ -24,6 +24,19 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return u >> 16;
 }
 
+// binary64 -> bf16 bit pattern, one rounding to nearest even (finite inputs).
+// Round to odd into binary32 first (truncate, then set the last bit when the
+// truncation was inexact), then to nearest even into bf16: with 16 spare
+// bits in between this equals the direct rounding (Boldo and Melquiond,
+// "Emulation of FMA and correctly rounded sums: proved algorithms using
+// rounding to odd").
+__device__ __forceinline__ uint32_t f64_to_bf16_rne(double m) {
+  const float f = __double2float_rz(m);
+  uint32_t u = __float_as_uint(f);
+  if ((double)f != m) u |= 1u;
+  return f32_to_bf16_rne(__uint_as_float(u));
+}
+
 // The int8 code of a quotient: round half away from zero, clamp to
 // [-127, 127]. roundf is C's round (ties away from zero).
 __device__ __forceinline__ int int8_code(float v) {

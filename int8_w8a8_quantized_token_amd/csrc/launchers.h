@@ -44,4 +44,19 @@ hipError_t launch_abs_histogram(const uint16_t* x, int64_t ldx, const float* smo
 hipError_t launch_calibrate_entropy(const uint32_t* hist, int64_t bins, const float* amax,
                                     float* scale, double* kl, hipStream_t s);
 
+// Fused producers (producers.hip).
+hipError_t launch_rmsnorm_quantize(uint16_t* h, int64_t ldh, const uint16_t* residual,
+                                   int64_t ldr, const float* g, float eps, int64_t M, int64_t K,
+                                   int8_t* q, int64_t ldq, float* s_tok, hipStream_t s);
+
+hipError_t launch_silu_mul_quantize(const uint16_t* gu, int64_t ldgu, const float* smooth,
+                                    int64_t M, int64_t I, int8_t* q, int64_t ldq, float* s_tok,
+                                    hipStream_t s);
+
+hipError_t launch_fold_gamma(const float* gamma, const float* smooth, int64_t K, float* g,
+                             hipStream_t s);
+
+hipError_t launch_residual_add(uint16_t* h, int64_t ldh, const uint16_t* r, int64_t ldr,
+                               int64_t M, int64_t K, hipStream_t s);
+
 }  // namespace w8a8

@@ -1,0 +1,367 @@
+// Fused producers on gfx950: the ops that feed a Llama block's linears end in
+// the per-token quantizer, so they emit int8 codes and scales directly
+// instead of a bf16 tensor that a separate quantize pass would read again.
+//
+// The Red Hat article "Understanding W8A8 INT8 LLM quantization: Half the
+// size, better performance, same accuracy" places the activation outliers in
+// RMSNorm's weight (section "How SmoothQuant prevents outliers in activation
+// tensors") and folds the SmoothQuant division into that weight (section
+// "How the SmoothQuant smoothing factor is computed"). So:
+//   * add + RMSNorm + quantize: h = bf16(h + r) (optional, written back as the
+//     new residual stream); ms = sum(h^2) / K rounded once to binary32;
+//     inv = 1 / sqrt(ms + eps); y = (h * inv) * g with g = gamma / s; then
+//     S = max|y| / 127 and codes;
+//   * SiLU-gated product + quantize: m = bf16((g / (1 + exp(-g))) * u) in
+//     binary64 from the bf16 gate and up halves of a row; x' = m / s; codes.
+//
+// The sum of squares is exact per term (a bf16 square fits binary64) and is
+// accumulated with error-free transformations (two-sum, double-double), so
+// the rounded result does not depend on the summation order.
+
+#include "device_common.h"
+#include "launchers.h"
+
+namespace w8a8 {
+
+// ---------------------------------------------------------------------------
+// double-double accumulation
+// ---------------------------------------------------------------------------
+
+struct DD {
+  double hi, lo;
+};
+
+// s + e = a + b exactly (Knuth's two-sum; needs no contraction).
+__device__ __forceinline__ void two_sum(double a, double b, double& s, double& e) {
+  s = a + b;
+  const double bp = s - a;
+  e = (a - (s - bp)) + (b - bp);
+}
+
+__device__ __forceinline__ DD dd_add(DD x, DD y) {
+  double s, e;
+  two_sum(x.hi, y.hi, s, e);
+  e += x.lo + y.lo;
+  DD r;
+  two_sum(s, e, r.hi, r.lo);
+  return r;
+}
+
+__device__ __forceinline__ DD dd_add(DD x, double v) {
+  double s, e;
+  two_sum(x.hi, v, s, e);
+  DD r;
+  r.hi = s;
+  r.lo = x.lo + e;
+  return r;
+}
+
+__device__ __forceinline__ DD dd_shfl_xor(DD x, int off) {
+  DD r;
+  r.hi = __shfl_xor(x.hi, off, kWave);
+  r.lo = __shfl_xor(x.lo, off, kWave);
+  return r;
+}
+
+// Block-wide double-double sum; every thread gets hi + lo.
+template <int BS>
+__device__ __forceinline__ double block_sum_dd(DD v, DD* red) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = dd_add(v, dd_shfl_xor(v, off));
+  const int wave = threadIdx.x / kWave;
+  if ((threadIdx.x & (kWave - 1)) == 0) red[wave] = v;
+  __syncthreads();
+  DD t = red[0];
+#pragma unroll
+  for (int w = 1; w < BS / kWave; ++w) t = dd_add(t, red[w]);
+  return t.hi + t.lo;
+}
+
+template <int BS>
+__device__ __forceinline__ float block_max_f(float v, float* red) {
+  v = wave_max(v);
+  const int wave = threadIdx.x / kWave;
+  if ((threadIdx.x & (kWave - 1)) == 0) red[wave] = v;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int w = 1; w < BS / kWave; ++w) r = fmaxf(r, red[w]);
+  return r;
+}
+
+// Codes of 8 values of one row (as in the per-token quantizer).
+__device__ __forceinline__ void codes8(int8_t* __restrict__ qr, int vi, const float (&v)[8],
+                                       float S, float R, bool fast) {
+  int c[8];
+  if (S == 0.0f) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) c[e] = 0;
+  } else {
+    uint32_t slow = fast ? 0u : 0xFFu;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      bool ok;
+      c[e] = (int)code_fast(v[e], R, ok);
+      slow |= ok ? 0u : (1u << e);
+    }
+    if (slow != 0u) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (slow & (1u << e)) c[e] = int8_code(v[e] / S);
+    }
+  }
+  uint2 packed;
+  packed.x = pack4_i8(c[0], c[1], c[2], c[3]);
+  packed.y = pack4_i8(c[4], c[5], c[6], c[7]);
+  *reinterpret_cast<uint2*>(qr + (int64_t)vi * 8) = packed;
+}
+
+__device__ __forceinline__ void unpack8(uint4 raw, float (&v)[8]) {
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    v[2 * e] = bf16_lo(w[e]);
+    v[2 * e + 1] = bf16_hi(w[e]);
+  }
+}
+
+__device__ __forceinline__ uint4 pack8_bf16(const float (&v)[8]) {
+  uint4 r;
+  r.x = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
+  r.y = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
+  r.z = f32_to_bf16_rne(v[4]) | (f32_to_bf16_rne(v[5]) << 16);
+  r.w = f32_to_bf16_rne(v[6]) | (f32_to_bf16_rne(v[7]) << 16);
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// residual add + RMSNorm + quantize: one BS-thread workgroup per row, the row
+// in registers (NV vectors of 8 per thread)
+// ---------------------------------------------------------------------------
+
+template <int BS, int NV, bool ADD>
+__global__ __launch_bounds__(BS) void rmsnorm_quantize_kernel(
+    uint16_t* __restrict__ h, int64_t ldh, const uint16_t* __restrict__ res, int64_t ldr,
+    const float* __restrict__ g, float eps, int K, int8_t* __restrict__ q, int64_t ldq,
+    float* __restrict__ s_tok) {
+  __shared__ DD red_dd[BS / kWave];
+  __shared__ float red_f[BS / kWave];
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int nvec = K / 8;
+  uint16_t* hr = h + row * ldh;
+
+  float v[NV][8];
+  DD acc = {0.0, 0.0};
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int vi = tid + i * BS;
+    if (vi < nvec) {
+      unpack8(*reinterpret_cast<const uint4*>(hr + (int64_t)vi * 8), v[i]);
+      if constexpr (ADD) {
+        float r[8];
+        unpack8(*reinterpret_cast<const uint4*>(res + row * ldr + (int64_t)vi * 8), r);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[i][e] = __uint_as_float(f32_to_bf16_rne(v[i][e] + r[e]) << 16);
+        *reinterpret_cast<uint4*>(hr + (int64_t)vi * 8) = pack8_bf16(v[i]);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const double x = (double)v[i][e];
+        acc = dd_add(acc, x * x);
+      }
+    }
+  }
+  const double ss = block_sum_dd<BS>(acc, red_dd);
+  const float ms = (float)(ss / (double)K);
+  const float inv = 1.0f / sqrtf(ms + eps);
+
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int vi = tid + i * BS;
+    if (vi < nvec) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        v[i][e] = (v[i][e] * inv) * g[vi * 8 + e];
+        amax = fmaxf(amax, fabsf(v[i][e]));
+      }
+    }
+  }
+  amax = block_max_f<BS>(amax, red_f);
+  const float S = amax / kQMax;
+  if (tid == 0) s_tok[row] = S;
+  const bool fast = code_fast_ok(S);
+  const float R = fast ? 1.0f / S : 0.0f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int vi = tid + i * BS;
+    if (vi < nvec) codes8(q + row * ldq, vi, v[i], S, R, fast);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// SiLU-gated product + quantize
+// ---------------------------------------------------------------------------
+
+template <int BS, int NV, bool SMOOTH>
+__global__ __launch_bounds__(BS) void silu_mul_quantize_kernel(
+    const uint16_t* __restrict__ gu, int64_t ldgu, const float* __restrict__ smooth, int I,
+    int8_t* __restrict__ q, int64_t ldq, float* __restrict__ s_tok) {
+  __shared__ float red_f[BS / kWave];
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int nvec = I / 8;
+  const uint16_t* gr = gu + row * ldgu;
+
+  float v[NV][8];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int vi = tid + i * BS;
+    if (vi < nvec) {
+      float gv[8], uv[8];
+      unpack8(*reinterpret_cast<const uint4*>(gr + (int64_t)vi * 8), gv);
+      unpack8(*reinterpret_cast<const uint4*>(gr + I + (int64_t)vi * 8), uv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const double gd = (double)gv[e];
+        const double m = (gd / (1.0 + exp(-gd))) * (double)uv[e];
+        float mf = __uint_as_float((uint32_t)f64_to_bf16_rne(m) << 16);
+        if constexpr (SMOOTH) mf = mf / smooth[vi * 8 + e];
+        v[i][e] = mf;
+        amax = fmaxf(amax, fabsf(mf));
+      }
+    }
+  }
+  amax = block_max_f<BS>(amax, red_f);
+  const float S = amax / kQMax;
+  if (tid == 0) s_tok[row] = S;
+  const bool fast = code_fast_ok(S);
+  const float R = fast ? 1.0f / S : 0.0f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int vi = tid + i * BS;
+    if (vi < nvec) codes8(q + row * ldq, vi, v[i], S, R, fast);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// small elementwise helpers: gamma / s, and h = bf16(h + r)
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void fold_gamma_kernel(const float* __restrict__ gamma,
+                                                         const float* __restrict__ smooth,
+                                                         int64_t K, float* __restrict__ g) {
+  const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (k < K) g[k] = smooth ? gamma[k] / smooth[k] : gamma[k];
+}
+
+__global__ __launch_bounds__(256) void residual_add_kernel(uint16_t* __restrict__ h, int64_t ldh,
+                                                           const uint16_t* __restrict__ r,
+                                                           int64_t ldr, int64_t M, int K) {
+  const int vi = blockIdx.x * 256 + threadIdx.x;
+  if (vi >= K / 8) return;
+  for (int64_t m = blockIdx.y; m < M; m += gridDim.y) {
+    float a[8], b[8];
+    unpack8(*reinterpret_cast<const uint4*>(h + m * ldh + (int64_t)vi * 8), a);
+    unpack8(*reinterpret_cast<const uint4*>(r + m * ldr + (int64_t)vi * 8), b);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a[e] = a[e] + b[e];
+    *reinterpret_cast<uint4*>(h + m * ldh + (int64_t)vi * 8) = pack8_bf16(a);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+
+// Threads per row: 1024 for few rows (decode), otherwise 256 (512 for rows
+// longer than 8192 channels), raised until 8 vectors per thread cover the row.
+static int producer_threads(int64_t rows, int64_t K) {
+  int bs = rows <= 512 ? 1024 : (K > 8192 ? 512 : 256);
+  while (bs < 1024 && (K / 8 + bs - 1) / bs > 8) bs *= 2;
+  return bs;
+}
+
+template <int BS, bool ADD>
+static hipError_t launch_rmsnorm_bs(uint16_t* h, int64_t ldh, const uint16_t* r, int64_t ldr,
+                                    const float* g, float eps, int64_t M, int64_t K, int8_t* q,
+                                    int64_t ldq, float* s_tok, hipStream_t s) {
+  const int64_t per = (K / 8 + BS - 1) / BS;
+#define W8A8_RMS(NVV)                                                                             \
+  hipLaunchKernelGGL((rmsnorm_quantize_kernel<BS, NVV, ADD>), dim3((unsigned)M), dim3(BS), 0, s, \
+                     h, ldh, r, ldr, g, eps, (int)K, q, ldq, s_tok)
+  if (per <= 1) W8A8_RMS(1);
+  else if (per <= 2) W8A8_RMS(2);
+  else if (per <= 4) W8A8_RMS(4);
+  else W8A8_RMS(8);
+#undef W8A8_RMS
+  return hipGetLastError();
+}
+
+template <bool ADD>
+static hipError_t launch_rmsnorm_add(uint16_t* h, int64_t ldh, const uint16_t* r, int64_t ldr,
+                                     const float* g, float eps, int64_t M, int64_t K, int8_t* q,
+                                     int64_t ldq, float* s_tok, hipStream_t s) {
+  switch (producer_threads(M, K)) {
+    case 256: return launch_rmsnorm_bs<256, ADD>(h, ldh, r, ldr, g, eps, M, K, q, ldq, s_tok, s);
+    case 512: return launch_rmsnorm_bs<512, ADD>(h, ldh, r, ldr, g, eps, M, K, q, ldq, s_tok, s);
+    default: return launch_rmsnorm_bs<1024, ADD>(h, ldh, r, ldr, g, eps, M, K, q, ldq, s_tok, s);
+  }
+}
+
+hipError_t launch_rmsnorm_quantize(uint16_t* h, int64_t ldh, const uint16_t* residual,
+                                   int64_t ldr, const float* g, float eps, int64_t M, int64_t K,
+                                   int8_t* q, int64_t ldq, float* s_tok, hipStream_t s) {
+  return residual ? launch_rmsnorm_add<true>(h, ldh, residual, ldr, g, eps, M, K, q, ldq, s_tok, s)
+                  : launch_rmsnorm_add<false>(h, ldh, residual, ldr, g, eps, M, K, q, ldq, s_tok, s);
+}
+
+template <int BS, bool SMOOTH>
+static hipError_t launch_silu_bs(const uint16_t* gu, int64_t ldgu, const float* smooth, int64_t M,
+                                 int64_t I, int8_t* q, int64_t ldq, float* s_tok, hipStream_t s) {
+  const int64_t per = (I / 8 + BS - 1) / BS;
+#define W8A8_SILU(NVV)                                                                          \
+  hipLaunchKernelGGL((silu_mul_quantize_kernel<BS, NVV, SMOOTH>), dim3((unsigned)M), dim3(BS), \
+                     0, s, gu, ldgu, smooth, (int)I, q, ldq, s_tok)
+  if (per <= 1) W8A8_SILU(1);
+  else if (per <= 2) W8A8_SILU(2);
+  else if (per <= 4) W8A8_SILU(4);
+  else W8A8_SILU(8);
+#undef W8A8_SILU
+  return hipGetLastError();
+}
+
+template <bool SMOOTH>
+static hipError_t launch_silu_sm(const uint16_t* gu, int64_t ldgu, const float* smooth, int64_t M,
+                                 int64_t I, int8_t* q, int64_t ldq, float* s_tok, hipStream_t s) {
+  switch (producer_threads(M, I)) {
+    case 256: return launch_silu_bs<256, SMOOTH>(gu, ldgu, smooth, M, I, q, ldq, s_tok, s);
+    case 512: return launch_silu_bs<512, SMOOTH>(gu, ldgu, smooth, M, I, q, ldq, s_tok, s);
+    default: return launch_silu_bs<1024, SMOOTH>(gu, ldgu, smooth, M, I, q, ldq, s_tok, s);
+  }
+}
+
+hipError_t launch_silu_mul_quantize(const uint16_t* gu, int64_t ldgu, const float* smooth,
+                                    int64_t M, int64_t I, int8_t* q, int64_t ldq, float* s_tok,
+                                    hipStream_t s) {
+  return smooth ? launch_silu_sm<true>(gu, ldgu, smooth, M, I, q, ldq, s_tok, s)
+                : launch_silu_sm<false>(gu, ldgu, smooth, M, I, q, ldq, s_tok, s);
+}
+
+hipError_t launch_fold_gamma(const float* gamma, const float* smooth, int64_t K, float* g,
+                             hipStream_t s) {
+  hipLaunchKernelGGL(fold_gamma_kernel, dim3((unsigned)((K + 255) / 256)), dim3(256), 0, s, gamma,
+                     smooth, K, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_residual_add(uint16_t* h, int64_t ldh, const uint16_t* r, int64_t ldr,
+                               int64_t M, int64_t K, hipStream_t s) {
+  const dim3 grid((unsigned)((K / 8 + 255) / 256), (unsigned)(M < 65535 ? M : 65535));
+  hipLaunchKernelGGL(residual_add_kernel, grid, dim3(256), 0, s, h, ldh, r, ldr, M, (int)K);
+  return hipGetLastError();
+}
+
+}  // namespace w8a8

@@ -23,7 +23,7 @@ def lib():
 
 def test_exports_every_header_function(lib):
     names = W.header_functions()
-    assert len(names) == 15
+    assert len(names) == 19
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
@@ -151,6 +151,29 @@ def test_static_scale_validation(lib):
     assert ce(None, 2048, A, A, None, None) == INVALID
     assert ce(A, 2048, A, None, None, None) == INVALID
     assert ce(A, 2048, A, A, A + 4, None) == MISALIGNED                         # kl alignment
+
+
+def test_producer_validation(lib):
+    rq = lib.w8a8_rmsnorm_quantize
+    assert rq(A, 4096, None, 4096, A, 1e-5, 16, 4096, A, 4096, None, None) == INVALID   # s_tok
+    assert rq(A, 4096, None, 4096, A, -1.0, 16, 4096, A, 4096, A, None) == INVALID      # eps
+    assert rq(A, 4096, None, 4096, A, float("nan"), 16, 4096, A, 4096, A, None) == INVALID
+    assert rq(A, 4096, None, 4096, A, 1e-5, 16, 4104, A, 4104, A, None) == UNSUPPORTED
+    assert rq(A, 65552, None, 65552, A, 1e-5, 1, 65552, A, 65552, A, None) == UNSUPPORTED
+    assert rq(A, 4096, MIS, 4096, A, 1e-5, 16, 4096, A, 4096, A, None) == MISALIGNED
+    assert rq(None, 4096, None, 4096, None, 1e-5, 0, 4096, None, 4096, None, None) == OK
+    sq = lib.w8a8_silu_mul_quantize
+    assert sq(A, 8192, None, 16, 4096, A, 4096, None, None) == INVALID
+    assert sq(A, 8000, None, 16, 4096, A, 4096, A, None) == INVALID                 # ld < 2I
+    assert sq(A, 8192, None, 16, 4104, A, 4104, A, None) == UNSUPPORTED
+    assert sq(None, 8192, None, 0, 4096, None, 4096, None, None) == OK
+    fg = lib.w8a8_fold_gamma
+    assert fg(None, None, 16, A, None) == INVALID
+    assert fg(None, None, 0, None, None) == OK
+    ra = lib.w8a8_residual_add
+    assert ra(A, 4096, None, 4096, 16, 4096, None) == INVALID
+    assert ra(A, 12, A, 12, 16, 12, None) == UNSUPPORTED
+    assert ra(None, 4096, None, 4096, 0, 4096, None) == OK
 
 
 def test_python_binding_raises_typed_error(lib):
