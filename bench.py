@@ -41,6 +41,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true",
                    help="skip timing the CPU oracle")
     p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--no-chain", action="store_true", help="skip the 32-layer block chain")
     p.add_argument("--detail", action="store_true", help="per-shape timings on stderr")
     p.add_argument("--counters", action="store_true",
                    help="eager launches for hardware-counter runs (rocprofv3 --pmc); no timing")
@@ -246,6 +247,77 @@ def counters(torch, S, ms, layers=4):
     log("[counters] 3 x 1 GiB device copies")
 
 
+CHAIN_M = 3000
+
+
+def run_chain(torch, W, WL, S, args):
+    """The Llama-shaped block chain: 32 layers on 3000 tokens, every
+    activation entering a linear produced as int8 codes by a fused producer
+    (residual add + RMSNorm with the smoothing folded into its weight,
+    SiLU-gated product), the q slice of qkv standing in for attention.
+    Weights are the decode setup's distinct per-layer buffers."""
+    dev = "cuda"
+    M, hid, inter = CHAIN_M, 4096, 14336
+    shp = {p: (n, k) for p, n, k in S.shapes}
+    outl = WL.outlier_channels(hid, 0.01, "llama8b_chain")
+    gamma = torch.ones(hid, dtype=torch.float32, device=dev)
+    gamma[torch.from_numpy(outl).to(dev)] = 20.0
+    g_attn = W.w8a8_fold_gamma(gamma, S.s["qkv"])
+    g_mlp = W.w8a8_fold_gamma(gamma, S.s["gate_up"])
+    x0 = S.bf16(WL.activations(M, hid, "llama8b_chain", "x", outliers=outl))
+    h = torch.empty_like(x0)
+    y = {p: torch.empty((M, shp[p][0]), dtype=torch.bfloat16, device=dev) for p in shp}
+    xq = torch.empty((M, inter), dtype=torch.int8, device=dev)
+    st = torch.empty((M,), dtype=torch.float32, device=dev)
+
+    def q_view(k):
+        return xq[:, :k]
+
+    def layers(with_gemm):
+        h.copy_(x0)
+        pending = None
+        for layer in range(LAYERS):
+            W.w8a8_rmsnorm_quantize(h, g_attn, 1e-5, residual=pending, xq=q_view(hid), s_tok=st)
+            if with_gemm:
+                W.w8a8_gemm(q_view(hid), st, S.wq["qkv"][layer], S.sw["qkv"], y=y["qkv"])
+            W.w8a8_quantize_act(y["qkv"][:, :hid], S.s["o"], xq=q_view(hid), s_tok=st)
+            if with_gemm:
+                W.w8a8_gemm(q_view(hid), st, S.wq["o"][layer], S.sw["o"], y=y["o"])
+            W.w8a8_rmsnorm_quantize(h, g_mlp, 1e-5, residual=y["o"], xq=q_view(hid), s_tok=st)
+            if with_gemm:
+                W.w8a8_gemm(q_view(hid), st, S.wq["gate_up"][layer], S.sw["gate_up"],
+                            y=y["gate_up"])
+            W.w8a8_silu_mul_quantize(y["gate_up"], S.s["down"], xq=xq, s_tok=st)
+            if with_gemm:
+                W.w8a8_gemm(xq, st, S.wq["down"][layer], S.sw["down"], y=y["down"])
+            pending = y["down"]
+        W.w8a8_residual_add(h, pending)
+
+    for v in y.values():
+        v.zero_()
+    g_full = capture(torch, lambda: layers(True))
+    t_full = time_graph(torch, g_full, max(args.steps // 4, 3), min(args.warmup, 2))
+    del g_full
+    g_prod = capture(torch, lambda: layers(False))
+    t_prod = time_graph(torch, g_prod, max(args.steps // 4, 3), min(args.warmup, 2))
+    del g_prod
+    ops = sum(2 * M * n * k for n, k in shp.values()) * LAYERS
+    # producer bytes per layer: two norms (read h and the residual, write h,
+    # write codes), the q-slice quantizer, the SiLU product (read gate|up,
+    # write codes); scales and vectors are negligible
+    pbytes = LAYERS * (2 * (2 * M * hid * 3 + M * hid) + (2 * M * hid + M * hid)
+                       + (2 * M * 2 * inter + M * inter))
+    tops = ops / (t_full * 1e-3) / 1e12
+    log(f"[bench] chain: 32 layers x {M} tokens {t_full:.3f} ms ({tops:.0f} TOPS); "
+        f"producers alone {t_prod:.3f} ms ({pbytes / (t_prod * 1e-3) / 1e9:.0f} GB/s)")
+    return {"value": round(tops, 1), "unit": "TOPS", "ms_per_forward": round(t_full, 4),
+            "producers_ms": round(t_prod, 4),
+            "producers_GBps": round(pbytes / (t_prod * 1e-3) / 1e9, 1),
+            "config": {"workload": "llama8b_chain: 32 layers x (fused norm/SiLU producers + "
+                                   "4 W8A8 GEMMs), 3000 tokens, q slice for attention",
+                       "tokens": M}}
+
+
 def cpu_baseline(W, WL, sample_ms, min_seconds=10.0):
     """The oracle, timed on this host on one layer of the decode workload."""
     import numpy as np
@@ -354,6 +426,9 @@ def main():
         "value": round(s_value, 1), "unit": "GB/s", "ms_per_step": round(s_step, 4),
         "config": {"workload": "llama8b_decode as above, w8a8_linear_static with one "
                                "entropy-calibrated activation scale per projection"}}
+
+    if not args.no_chain:
+        out["chain"] = run_chain(torch, W, WL, S, args)
 
     if not args.no_prefill:
         p_step, p_gemm, p_launch, p_per = run_phase(torch, S, (PREFILL_M,), max(args.steps // 4, 3),
