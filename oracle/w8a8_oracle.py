@@ -544,3 +544,64 @@ def chain_forward(x_bf16: np.ndarray, layers, eps=1e-5):
         q, S = silu_mul_quantize(y_gu, L["s_down"])
         pending = lin(q, S, L["down"])
     return residual_add(h, pending) if pending is not None else h
+
+
+# ---------------------------------------------------------------------------
+# GPTQ: weight quantization with error compensation ([HALF])
+# ---------------------------------------------------------------------------
+#
+# [HALF] "The solution: How GPTQ improves on naive quantization" quantizes a
+# layer's weights one input column at a time and, after each, pushes the
+# rounding error onto the columns not yet quantized, weighted by the inverse
+# of the Hessian H = 2 X^T X of the calibration activations (the paper the
+# page cites, Frantar et al. 2022, gives the update through the upper
+# Cholesky factor U of H^-1). Readings:
+#   * X are the smoothed calibration activations x' = x / s (binary32, then
+#     binary64); H = 2 X^T X in binary64;
+#   * damping: H + lambda I with lambda = 0.01 * mean(diag H); a column never
+#     excited (H_jj = 0) gets H_jj = 1 first;
+#   * columns in their natural order; one scale per output channel, the RTN
+#     scale max|W'| / 127 of the smoothed bf16 weights, fixed beforehand;
+#   * the code of column j is the RTN rule applied to the binary32 value of
+#     the updated weight: clamp(round(RN32(w) / s)) in binary32, round half
+#     away; then err = (w - q s) / U_jj and w_k -= err * U_jk for k > j, in
+#     binary64, a product then a difference (no fused multiply-add).
+
+GPTQ_DAMP = 0.01
+
+
+def gptq_hessian(x_bf16: np.ndarray, smooth=None) -> np.ndarray:
+    """H = 2 X'^T X' (float64 [K, K]) of smoothed calibration activations."""
+    xs = smooth_activations(bf16_to_f32(x_bf16), smooth).astype(np.float64)
+    return 2.0 * (xs.T @ xs)
+
+
+def gptq_factor(H: np.ndarray, damp: float = GPTQ_DAMP) -> np.ndarray:
+    """U, upper triangular with H_damped^-1 = U^T U (float64 [K, K])."""
+    H = np.array(H, dtype=np.float64, copy=True)
+    d = np.diag(H).copy()
+    d[d == 0] = 1.0
+    np.fill_diagonal(H, d)
+    H[np.diag_indices_from(H)] += damp * float(np.mean(d))
+    Hinv = np.linalg.inv(H)
+    Hinv = 0.5 * (Hinv + Hinv.T)
+    return np.linalg.cholesky(Hinv).T
+
+
+def gptq_quantize(w_bf16: np.ndarray, smooth, U: np.ndarray):
+    """GPTQ codes of a weight [N, K] given the factor U. Returns
+    (Wq int8 [N, K], sw float32 [N]); the scales are RTN's."""
+    wb = smooth_weight(w_bf16, smooth)
+    w32 = bf16_to_f32(wb)
+    sw = absmax_scale(w32, axis=1)
+    W = w32.astype(np.float64)
+    N, K = W.shape
+    q = np.zeros((N, K), np.int8)
+    s64 = sw.astype(np.float64)
+    for j in range(K):
+        qj = quantize_with_scale(W[:, j].astype(F32)[:, None], sw[:, None])[:, 0]
+        q[:, j] = qj
+        err = (W[:, j] - qj.astype(np.float64) * s64) / U[j, j]
+        if j + 1 < K:
+            W[:, j + 1:] -= np.outer(err, U[j, j + 1:])
+    return q, sw

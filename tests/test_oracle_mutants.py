@@ -180,6 +180,31 @@ def _silu_halves_swapped(gu_bf16):
 _real_silu_mul = O.silu_mul
 
 
+def _gptq_no_feedback(w_bf16, smooth, U):                 # plain RTN
+    return O.prepare_weight(w_bf16, smooth)
+
+
+def _gptq_error_sign(w_bf16, smooth, U):
+    wb = O.smooth_weight(w_bf16, smooth)
+    w32 = O.bf16_to_f32(wb)
+    sw = O.absmax_scale(w32, axis=1)
+    W = w32.astype(np.float64)
+    q = np.zeros(W.shape, np.int8)
+    for j in range(W.shape[1]):
+        qj = O.quantize_with_scale(W[:, j].astype(F32)[:, None], sw[:, None])[:, 0]
+        q[:, j] = qj
+        err = (W[:, j] - qj * sw.astype(np.float64)) / U[j, j]
+        W[:, j + 1:] += np.outer(err, U[j, j + 1:])
+    return q, sw
+
+
+def _gptq_factor_lower(H, damp=O.GPTQ_DAMP):                # H^-1 = L L^T, L used as U
+    return _real_gptq_factor(H, damp).T
+
+
+_real_gptq_factor = O.gptq_factor
+
+
 MUTANTS = {
     "ties_to_even": ("round_half_away", _rint_round),
     "ties_toward_plus_inf": ("round_half_away", _ceil_ties),
@@ -208,6 +233,9 @@ MUTANTS = {
     "fold_gamma_multiplies": ("fold_gamma", _fold_gamma_multiplies),
     "rmsnorm_drops_residual": ("rmsnorm_quantize", _rmsnorm_drops_residual),
     "silu_halves_swapped": ("silu_mul", _silu_halves_swapped),
+    "gptq_no_feedback": ("gptq_quantize", _gptq_no_feedback),
+    "gptq_error_sign": ("gptq_quantize", _gptq_error_sign),
+    "gptq_factor_lower": ("gptq_factor", _gptq_factor_lower),
 }
 
 PINS = [getattr(P, n) for n in dir(P)
