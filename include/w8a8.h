@@ -307,6 +307,54 @@ w8a8_status_t w8a8_fold_gamma(const float* gamma, const float* smooth, int64_t K
 w8a8_status_t w8a8_residual_add(uint16_t* h, int64_t ldh, const uint16_t* r, int64_t ldr,
                                 int64_t M, int64_t K, hipStream_t stream);
 
+/* ----------------------------------------------------------------------- *
+ * GPTQ weight quantization (offline). Part 1, section "The solution: How
+ * GPTQ improves on naive quantization": quantize one input column at a time
+ * and push each rounding error onto the columns not yet quantized, weighted
+ * by the Hessian of the calibration activations. Produces the same Wq and
+ * per-output-channel scales as w8a8_quantize_weight (the scales are equal;
+ * the codes differ where errors were compensated).
+ * ----------------------------------------------------------------------- */
+
+/*
+ * H[i,j] += 2 sum_m x'[m,i] x'[m,j], x' = x / smooth (binary32, then binary64).
+ *   x [n, K] bf16, ldx >= K; smooth [K] or NULL (read);
+ *   H [K, K] fp64 row-major, dense (read and written; zero it first).
+ *   K % 16 == 0, K <= 32768.
+ */
+w8a8_status_t w8a8_gptq_hessian(const uint16_t* x, int64_t ldx, const float* smooth, int64_t n,
+                                int64_t K, double* H, hipStream_t stream);
+
+/* Workspace for w8a8_gptq_factor: K*K + 1 doubles, 256-byte aligned size. */
+size_t w8a8_gptq_factor_workspace_bytes(int64_t K);
+
+/*
+ * U, upper triangular, with U^T U = (Hd + lambda I)^-1, where Hd is H with
+ * zero diagonal entries set to 1 and lambda = damp * mean(diag Hd) (damp
+ * 0.01 is customary). Computed as U = J inv(chol(J (Hd + lambda I) J)) J
+ * (J reverses the index order), in binary64.
+ *   H [K, K] fp64 (read); U [K, K] fp64 (written); workspace as sized above.
+ */
+w8a8_status_t w8a8_gptq_factor(const double* H, int64_t K, double damp, double* U,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace for w8a8_gptq_quantize: N*K + 64*N doubles (256-byte aligned parts). */
+size_t w8a8_gptq_quantize_workspace_bytes(int64_t N, int64_t K);
+
+/*
+ * GPTQ codes of w [N, K]: W' = bf16(w * smooth) as in w8a8_quantize_weight,
+ * s_chan[n] = max_k |W'[n,k]| / 127, then for columns j = 0 .. K-1 of every
+ * row: q = clamp(round(RN32(W'[n,j]) / s_chan[n]), -127, 127) (binary32,
+ * half away), err = (W'[n,j] - q s_chan[n]) / U[j,j], and
+ * W'[n,k] -= err * U[j,k] for k > j (binary64 product, then difference).
+ *   w [N, K] bf16, ldw >= K; smooth [K] or NULL; U [K, K] fp64 (read)
+ *   wq [N, K] int8, ldwq >= K; s_chan [N] fp32 (written)
+ */
+w8a8_status_t w8a8_gptq_quantize(const uint16_t* w, int64_t ldw, const float* smooth,
+                                 const double* U, int64_t N, int64_t K, int8_t* wq, int64_t ldwq,
+                                 float* s_chan, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -19,6 +19,11 @@ from .binding import (  # noqa: F401
     w8a8_fold_gamma,
     w8a8_gemm,
     w8a8_gemm_i32,
+    w8a8_gptq_factor,
+    w8a8_gptq_factor_workspace_bytes,
+    w8a8_gptq_hessian,
+    w8a8_gptq_quantize,
+    w8a8_gptq_quantize_workspace_bytes,
     w8a8_linear,
     w8a8_linear_static,
     w8a8_linear_workspace_bytes,

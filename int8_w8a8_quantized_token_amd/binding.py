@@ -51,6 +51,11 @@ _SIGNATURES = {
     "w8a8_silu_mul_quantize": (_i, [_p, _i64, _p, _i64, _i64, _p, _i64, _p, _p]),
     "w8a8_fold_gamma": (_i, [_p, _p, _i64, _p, _p]),
     "w8a8_residual_add": (_i, [_p, _i64, _p, _i64, _i64, _i64, _p]),
+    "w8a8_gptq_hessian": (_i, [_p, _i64, _p, _i64, _i64, _p, _p]),
+    "w8a8_gptq_factor_workspace_bytes": (_sz, [_i64]),
+    "w8a8_gptq_factor": (_i, [_p, _i64, ctypes.c_double, _p, _p, _sz, _p]),
+    "w8a8_gptq_quantize_workspace_bytes": (_sz, [_i64, _i64]),
+    "w8a8_gptq_quantize": (_i, [_p, _i64, _p, _p, _i64, _i64, _p, _i64, _p, _p, _sz, _p]),
 }
 
 HIST_BINS = 2048       # W8A8_HIST_BINS
@@ -393,3 +398,68 @@ def w8a8_residual_add(h, r, stream=None):
     pr, ldr = _mat(r, _bf16_types(), "r")
     _check(lib().w8a8_residual_add(ph, ldh, pr, ldr, M, K, _stream(stream)), "w8a8_residual_add")
     return h
+
+
+# ---------------------------------------------------------------------------
+# GPTQ
+# ---------------------------------------------------------------------------
+
+def _dense_f64(t, name):
+    torch = _torch()
+    if t.dtype != torch.float64 or not t.is_contiguous() or t.device.type != "cuda":
+        raise TypeError(f"{name}: need a contiguous float64 device tensor")
+    return t.data_ptr()
+
+
+def w8a8_gptq_hessian(x, smooth=None, H=None, stream=None):
+    """H [K, K] float64 += 2 x'^T x' (zero-initialized when not given)."""
+    torch = _torch()
+    n, K = x.shape
+    if H is None:
+        H = torch.zeros((K, K), dtype=torch.float64, device=x.device)
+    px, ldx = _mat(x, _bf16_types(), "x")
+    _check(lib().w8a8_gptq_hessian(px, ldx, _vec(smooth, "smooth"), n, K, _dense_f64(H, "H"),
+                                   _stream(stream)), "w8a8_gptq_hessian")
+    return H
+
+
+def w8a8_gptq_factor_workspace_bytes(K: int) -> int:
+    return lib().w8a8_gptq_factor_workspace_bytes(K)
+
+
+def w8a8_gptq_factor(H, damp=0.01, U=None, workspace=None, stream=None):
+    """U [K, K] float64, upper, U^T U = (H + lambda I)^-1."""
+    torch = _torch()
+    K = H.shape[0]
+    if U is None:
+        U = torch.empty((K, K), dtype=torch.float64, device=H.device)
+    nbytes = w8a8_gptq_factor_workspace_bytes(K)
+    if workspace is None:
+        workspace = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=H.device)
+    _check(lib().w8a8_gptq_factor(_dense_f64(H, "H"), K, float(damp), _dense_f64(U, "U"),
+                                  workspace.data_ptr(), workspace.numel(), _stream(stream)),
+           "w8a8_gptq_factor")
+    return U
+
+
+def w8a8_gptq_quantize_workspace_bytes(N: int, K: int) -> int:
+    return lib().w8a8_gptq_quantize_workspace_bytes(N, K)
+
+
+def w8a8_gptq_quantize(w, smooth, U, wq=None, s_chan=None, workspace=None, stream=None):
+    """w bf16 [N, K] -> (wq int8 [N, K], s_chan fp32 [N]) with GPTQ error feedback."""
+    torch = _torch()
+    N, K = w.shape
+    if wq is None:
+        wq = torch.empty((N, K), dtype=torch.int8, device=w.device)
+    if s_chan is None:
+        s_chan = torch.empty((N,), dtype=torch.float32, device=w.device)
+    nbytes = w8a8_gptq_quantize_workspace_bytes(N, K)
+    if workspace is None:
+        workspace = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=w.device)
+    pw, ldw = _mat(w, _bf16_types(), "w")
+    pq, ldq = _mat(wq, (torch.int8,), "wq")
+    _check(lib().w8a8_gptq_quantize(pw, ldw, _vec(smooth, "smooth"), _dense_f64(U, "U"), N, K,
+                                    pq, ldq, _vec(s_chan, "s_chan"), workspace.data_ptr(),
+                                    workspace.numel(), _stream(stream)), "w8a8_gptq_quantize")
+    return wq, s_chan

@@ -274,6 +274,70 @@ w8a8_status_t w8a8_residual_add(uint16_t* h, int64_t ldh, const uint16_t* r, int
   return from_hip(w8a8::launch_residual_add(h, ldh, r, ldr, M, K, stream));
 }
 
+// GPTQ -------------------------------------------------------------------
+
+constexpr int64_t kGptqMaxK = 32768;   // K x K binary64 factor: 8 GiB at the limit
+constexpr int64_t kGptqPanel = 64;
+
+w8a8_status_t w8a8_gptq_hessian(const uint16_t* x, int64_t ldx, const float* smooth, int64_t n,
+                                int64_t K, double* H, hipStream_t stream) {
+  W8A8_TRY(check_dims(n, K));
+  if (K > kGptqMaxK) return W8A8_ERROR_UNSUPPORTED;
+  if (n == 0) return W8A8_SUCCESS;
+  W8A8_TRY(check_matrix(x, ldx, n, K, 2));
+  if (smooth) W8A8_TRY(check_vector(smooth));
+  if (H == nullptr) return W8A8_ERROR_INVALID_VALUE;
+  if (!aligned(H, 8)) return W8A8_ERROR_MISALIGNED;
+  return from_hip(w8a8::launch_gptq_hessian(x, ldx, smooth, n, K, H, stream));
+}
+
+size_t w8a8_gptq_factor_workspace_bytes(int64_t K) {
+  if (K <= 0 || K > kGptqMaxK) return 0;
+  return align256((size_t)(K * K + 1) * sizeof(double));
+}
+
+w8a8_status_t w8a8_gptq_factor(const double* H, int64_t K, double damp, double* U,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (K <= 0 || H == nullptr || U == nullptr || !(damp >= 0.0) || damp > 1.0e6)
+    return W8A8_ERROR_INVALID_VALUE;
+  if (K > kGptqMaxK) return W8A8_ERROR_UNSUPPORTED;
+  if (!aligned(H, 8) || !aligned(U, 8)) return W8A8_ERROR_MISALIGNED;
+  if (workspace == nullptr || workspace_bytes < w8a8_gptq_factor_workspace_bytes(K))
+    return W8A8_ERROR_WORKSPACE;
+  if (!aligned(workspace, 256)) return W8A8_ERROR_MISALIGNED;
+  return from_hip(
+      w8a8::launch_gptq_factor(H, K, damp, U, static_cast<double*>(workspace), stream));
+}
+
+size_t w8a8_gptq_quantize_workspace_bytes(int64_t N, int64_t K) {
+  if (N <= 0 || K <= 0 || K > kGptqMaxK || N > kMaxDim) return 0;
+  return align256((size_t)N * (size_t)K * sizeof(double)) +
+         align256((size_t)N * kGptqPanel * sizeof(double));
+}
+
+w8a8_status_t w8a8_gptq_quantize(const uint16_t* w, int64_t ldw, const float* smooth,
+                                 const double* U, int64_t N, int64_t K, int8_t* wq, int64_t ldwq,
+                                 float* s_chan, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream) {
+  W8A8_TRY(check_dims(N, K));
+  if (K > kGptqMaxK) return W8A8_ERROR_UNSUPPORTED;
+  if (N == 0) return W8A8_SUCCESS;
+  W8A8_TRY(check_matrix(w, ldw, N, K, 2));
+  W8A8_TRY(check_matrix(wq, ldwq, N, K, 1));
+  W8A8_TRY(check_vector(s_chan));
+  if (smooth) W8A8_TRY(check_vector(smooth));
+  if (U == nullptr) return W8A8_ERROR_INVALID_VALUE;
+  if (!aligned(U, 8)) return W8A8_ERROR_MISALIGNED;
+  if (workspace == nullptr || workspace_bytes < w8a8_gptq_quantize_workspace_bytes(N, K))
+    return W8A8_ERROR_WORKSPACE;
+  if (!aligned(workspace, 256)) return W8A8_ERROR_MISALIGNED;
+  double* Wf = static_cast<double*>(workspace);
+  double* Err = reinterpret_cast<double*>(static_cast<char*>(workspace) +
+                                          align256((size_t)N * (size_t)K * sizeof(double)));
+  return from_hip(w8a8::launch_gptq_quantize(w, ldw, smooth, U, N, K, wq, ldwq, s_chan, Wf, Err,
+                                             stream));
+}
+
 w8a8_status_t w8a8_channel_absmax(const uint16_t* a, int64_t lda, int64_t rows, int64_t K,
                                   float* absmax, hipStream_t stream) {
   if (rows < 0 || K <= 0) return W8A8_ERROR_INVALID_VALUE;

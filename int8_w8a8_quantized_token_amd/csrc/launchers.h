@@ -59,4 +59,15 @@ hipError_t launch_fold_gamma(const float* gamma, const float* smooth, int64_t K,
 hipError_t launch_residual_add(uint16_t* h, int64_t ldh, const uint16_t* r, int64_t ldr,
                                int64_t M, int64_t K, hipStream_t s);
 
+// GPTQ (gptq.hip).
+hipError_t launch_gptq_hessian(const uint16_t* x, int64_t ldx, const float* smooth, int64_t n,
+                               int64_t K, double* H, hipStream_t s);
+
+hipError_t launch_gptq_factor(const double* H, int64_t K, double damp, double* U, double* work,
+                              hipStream_t s);
+
+hipError_t launch_gptq_quantize(const uint16_t* w, int64_t ldw, const float* smooth,
+                                const double* U, int64_t N, int64_t K, int8_t* wq, int64_t ldwq,
+                                float* s_chan, double* Wf, double* Err, hipStream_t s);
+
 }  // namespace w8a8

@@ -23,7 +23,7 @@ def lib():
 
 def test_exports_every_header_function(lib):
     names = W.header_functions()
-    assert len(names) == 19
+    assert len(names) == 24
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
@@ -174,6 +174,28 @@ def test_producer_validation(lib):
     assert ra(A, 4096, None, 4096, 16, 4096, None) == INVALID
     assert ra(A, 12, A, 12, 16, 12, None) == UNSUPPORTED
     assert ra(None, 4096, None, 4096, 0, 4096, None) == OK
+
+
+def test_gptq_validation(lib):
+    gh = lib.w8a8_gptq_hessian
+    assert gh(A, 4096, None, 16, 4096, None, None) == INVALID                 # no H
+    assert gh(A, 4096, None, 16, 4096, A + 4, None) == MISALIGNED
+    assert gh(A, 40000, None, 16, 40000, A, None) == UNSUPPORTED            # K > 32768
+    assert gh(None, 4096, None, 0, 4096, None, None) == OK
+    assert lib.w8a8_gptq_factor_workspace_bytes(0) == 0
+    assert lib.w8a8_gptq_factor_workspace_bytes(64) == (64 * 64 + 1) * 8 + (256 - (64 * 64 + 1) * 8 % 256)
+    gf = lib.w8a8_gptq_factor
+    assert gf(A, 64, 0.01, A, None, 0, None) == WORKSPACE
+    assert gf(A, 64, -1.0, A, A, 1 << 20, None) == INVALID
+    assert gf(A, 0, 0.01, A, A, 1 << 20, None) == INVALID
+    assert gf(A, 64, 0.01, A, A + 16, 1 << 20, None) == MISALIGNED
+    gq = lib.w8a8_gptq_quantize
+    wsb = lib.w8a8_gptq_quantize_workspace_bytes(16, 64)
+    assert wsb == 16 * 64 * 8 + 16 * 64 * 8
+    assert gq(A, 64, None, A, 16, 64, A, 64, A, A, wsb - 1, None) == WORKSPACE
+    assert gq(A, 64, None, None, 16, 64, A, 64, A, A, wsb, None) == INVALID
+    assert gq(A, 64, None, A, 16, 72, A, 72, A, A, 1 << 20, None) == UNSUPPORTED  # K % 16
+    assert gq(None, 64, None, None, 0, 64, None, 64, None, None, 0, None) == OK
 
 
 def test_python_binding_raises_typed_error(lib):
