@@ -882,6 +882,7 @@ static hipError_t launch_gemm_t(const int8_t* xq, int64_t ldq, const float* s_to
     const bool wide = N > 8192, mid = N > 4096 && N <= 8192, deep = K > 8192;
     if (M <= 4) {
       if (mid) W8A8_SKINNY(1, 2, 8, 8, false);
+      else if (wide || deep) W8A8_SKINNY(1, 1, 16, 2, false);
       else W8A8_SKINNY(1, 1, 16, 8, false);
     } else if (M <= 16) {
       if (wide) W8A8_SKINNY(1, 4, 8, 2, false);
