@@ -75,6 +75,31 @@ __device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
          ((uint32_t)(c & 0xFF) << 16) | ((uint32_t)(d & 0xFF) << 24);
 }
 
+// Codes of 8 values under one row scale S, packed little-endian (value e in
+// byte e). R = RN(1 / S) and fast = code_fast_ok(S); values the fast form
+// leaves open (all of them when fast is false) are divided. S == 0 gives 0.
+__device__ __forceinline__ uint2 codes8(const float (&v)[8], float S, float R, bool fast) {
+  int c[8];
+  if (S == 0.0f) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) c[e] = 0;
+  } else {
+    uint32_t slow = fast ? 0u : 0xFFu;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      bool ok;
+      c[e] = (int)code_fast(v[e], R, ok);
+      slow |= ok ? 0u : (1u << e);
+    }
+    if (slow != 0u) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (slow & (1u << e)) c[e] = int8_code(v[e] / S);
+    }
+  }
+  return uint2{pack4_i8(c[0], c[1], c[2], c[3]), pack4_i8(c[4], c[5], c[6], c[7])};
+}
+
 // Max over a wavefront (all 64 lanes end with the result).
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

@@ -29,57 +29,10 @@
 //   32x32: i = 8*(e/4) + 4*(l/32) + (e%4).
 
 #include "device_common.h"
+#include "gemm_common.h"
 #include "launchers.h"
 
 namespace w8a8 {
-
-__device__ __forceinline__ v4i ldg16(const int8_t* p) {
-  return *reinterpret_cast<const v4i*>(p);
-}
-
-__device__ __forceinline__ float dequant(int acc, float st, float sc) {
-  return ((float)acc * st) * sc;
-}
-
-// Writes 4 consecutive outputs of row m starting at column n (n % 4 == 0):
-// int32 accumulators, or bf16((float(acc) * st) * sc[e]).
-// vec: the output rows allow one 8-byte (bf16) or 16-byte (int32) store
-// per group of 4 (checked on the host: base and row stride aligned).
-template <bool I32OUT>
-__device__ __forceinline__ void store4(uint16_t* __restrict__ y, int64_t ldy,
-                                       int32_t* __restrict__ c, int64_t ldc, int m, int n, int N,
-                                       bool vec, float st, const float (&sc)[4], int a0, int a1,
-                                       int a2, int a3) {
-  if constexpr (I32OUT) {
-    int32_t* p = c + (int64_t)m * ldc + n;
-    if (vec && n + 3 < N) {
-      *reinterpret_cast<v4i*>(p) = v4i{a0, a1, a2, a3};
-    } else {
-      const int a[4] = {a0, a1, a2, a3};
-      for (int e = 0; e < 4 && n + e < N; ++e) p[e] = a[e];
-    }
-  } else {
-    uint16_t* p = y + (int64_t)m * ldy + n;
-    const uint32_t b0 = f32_to_bf16_rne(dequant(a0, st, sc[0]));
-    const uint32_t b1 = f32_to_bf16_rne(dequant(a1, st, sc[1]));
-    const uint32_t b2 = f32_to_bf16_rne(dequant(a2, st, sc[2]));
-    const uint32_t b3 = f32_to_bf16_rne(dequant(a3, st, sc[3]));
-    if (vec && n + 3 < N) {
-      *reinterpret_cast<uint2*>(p) = uint2{b0 | (b1 << 16), b2 | (b3 << 16)};
-    } else {
-      const uint32_t b[4] = {b0, b1, b2, b3};
-      for (int e = 0; e < 4 && n + e < N; ++e) p[e] = (uint16_t)b[e];
-    }
-  }
-}
-
-// Loads the 4 channel scales of outputs n..n+3 (clamped to valid indices;
-// values for columns past N are never stored).
-__device__ __forceinline__ void load_chan4(const float* __restrict__ s_chan, int n, int N,
-                                           float (&sc)[4]) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e) sc[e] = s_chan[min(n + e, N - 1)];
-}
 
 // ---------------------------------------------------------------------------
 // Skinny kernel (decode): M <= 16*MT tokens. A workgroup owns 16*RW output
@@ -386,6 +339,9 @@ __device__ __forceinline__ int lds_swz(int row) { return ((row >> 1) ^ (row >> 2
 // s_waitcnt with vmcnt = n and the other counters left alone (gfx9 encoding).
 #define W8A8_WAIT_VM(n) \
   __builtin_amdgcn_s_waitcnt(((n) & 0xF) | ((((n) >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8))
+
+// s_waitcnt lgkmcnt(0) with the other counters left alone.
+#define W8A8_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt((0xF) | (3 << 14) | (0x7 << 4))
 
 __device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::: "memory"); }
 
@@ -799,6 +755,165 @@ __global__ __launch_bounds__(pf128::THREADS, 1) void gemm_prefill128_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Mid kernel (decode batches of 17..64 tokens, K % 128 == 0). The skinny
+// kernel's split of the work: a workgroup owns 16*RW output channels and all
+// 16*MT token rows, its NW waves take interleaved K stages of 128 bytes and
+// sum their partial tiles in LDS at the end. But each wave brings its
+// operands in through LDS with direct global -> LDS loads of whole 128-byte
+// lines (the token tile is most of the bytes once M > 16, and register
+// loads of its 64-byte fragment rows move half lines), NS stages deep in
+// a ring of stage buffers of its own. A wave reads only what it loaded, so
+// the K loop has no workgroup barrier, and no operand bytes wait in
+// registers: NS - 1 stages of every wave are in flight while it multiplies.
+//
+// Stage layout: W rows [16*RW][128 B] then X rows [16*MT][128 B]; row r's
+// 16-byte chunk c sits at slot c ^ swz8(r) (conflict-free reads of the
+// 16x16x64 fragments: lane l reads row l % 16, chunk 4 h + l / 16).
+// ---------------------------------------------------------------------------
+
+template <int MT, int RW, int NW, int NS>
+struct MidCfg {
+  static constexpr int kBK = 128;
+  static constexpr int kWBytes = 16 * RW * kBK, kXBytes = 16 * MT * kBK;
+  static constexpr int kStageBytes = kWBytes + kXBytes;
+  static constexpr int kDmaW = kWBytes / (kWave * 16), kDmaX = kXBytes / (kWave * 16);
+  static constexpr int kDma = kDmaW + kDmaX;              // DMA instructions per stage
+  static constexpr int kLdsBytes = NW * NS * kStageBytes;
+  static_assert(MT >= 1 && MT <= 4 && RW >= 1 && NW >= 1 && NS >= 2 && NS <= 4, "");
+  static_assert((NS - 1) * kDma <= 63, "vmcnt holds at most 63 outstanding loads");
+  static_assert(kLdsBytes <= 160 * 1024, "LDS");
+  static_assert(NW * RW * MT * kWave * 16 <= kLdsBytes, "partial tiles fit in the stage buffers");
+};
+
+// Waits until at most n * per DMA instructions of this wave are outstanding
+// (n < 4; s_waitcnt takes an immediate).
+template <int PER>
+__device__ __forceinline__ void wait_stages(int n) {
+  if (n >= 3) W8A8_WAIT_VM(3 * PER);
+  else if (n == 2) W8A8_WAIT_VM(2 * PER);
+  else if (n == 1) W8A8_WAIT_VM(PER);
+  else W8A8_WAIT_VM(0);
+  asm volatile("" ::: "memory");     // LDS reads stay below the wait
+}
+
+template <int MT, int RW, int NW, int NS, bool I32OUT>
+__global__ __launch_bounds__(NW * kWave) void gemm_mid_kernel(
+    const int8_t* __restrict__ xq, int64_t ldq, const float* __restrict__ s_tok,
+    const int8_t* __restrict__ wq, int64_t ldw, const float* __restrict__ s_chan, int M, int N,
+    int K, uint16_t* __restrict__ y, int64_t ldy, int32_t* __restrict__ c, int64_t ldc,
+    bool vec_out) {
+  using C = MidCfg<MT, RW, NW, NS>;
+  constexpr int BK = C::kBK, SB = C::kStageBytes, DW = C::kDmaW, DX = C::kDmaX;
+  __shared__ __attribute__((aligned(1024))) int8_t lds[C::kLdsBytes];
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int r = lane & 15, g = lane >> 4;
+  const int n0 = blockIdx.x * 16 * RW;
+
+  float st[MT], sc[RW][4];
+  if constexpr (!I32OUT) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) st[mt] = s_tok[min(mt * 16 + r, M - 1)];
+#pragma unroll
+    for (int rw = 0; rw < RW; ++rw) load_chan4(s_chan, n0 + 16 * rw + 4 * g, N, sc[rw]);
+  }
+
+  // DMA sources: instruction i fills chunks [64 i, 64 i + 64) of an operand
+  // tile; chunk p holds row p / 8, global chunk (p % 8) ^ swz8(p / 8). Rows
+  // past N or M read a valid row; their outputs are never stored.
+  const int8_t* wsrc[DW];
+  const int8_t* xsrc[DX];
+#pragma unroll
+  for (int i = 0; i < DW; ++i) {
+    const int p = i * kWave + lane;
+    wsrc[i] = wq + (int64_t)min(n0 + (p >> 3), N - 1) * ldw + ((p & 7) ^ lds_swz8(p >> 3)) * 16;
+  }
+#pragma unroll
+  for (int i = 0; i < DX; ++i) {
+    const int p = i * kWave + lane;
+    xsrc[i] = xq + (int64_t)min(p >> 3, M - 1) * ldq + ((p & 7) ^ lds_swz8(p >> 3)) * 16;
+  }
+  int8_t* const ring = lds + wave * NS * SB;
+  const uint32_t ring_addr = lds_addr(ring);
+  auto issue = [&](int stage, int slot) {
+    const uint32_t base = ring_addr + slot * SB;
+    const int64_t k0 = (int64_t)stage * BK;
+#pragma unroll
+    for (int i = 0; i < DW; ++i) dma16(wsrc[i] + k0, base + i * kWave * 16);
+#pragma unroll
+    for (int i = 0; i < DX; ++i) dma16(xsrc[i] + k0, base + C::kWBytes + i * kWave * 16);
+  };
+
+  int foff[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) foff[h] = r * BK + (((4 * h + g) ^ lds_swz8(r)) << 4);
+
+  v4i acc[RW][MT];
+#pragma unroll
+  for (int rw = 0; rw < RW; ++rw)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[rw][mt] = v4i{0, 0, 0, 0};
+
+  // This wave's stages: wave, wave + NW, ...; stage j sits in slot j % NS.
+  const int nst = K / BK;
+  const int nj = nst > wave ? (nst - wave + NW - 1) / NW : 0;
+#pragma unroll
+  for (int j = 0; j < NS - 1; ++j)
+    if (j < nj) issue(wave + j * NW, j);
+  for (int j = 0; j < nj; ++j) {
+    if (j + NS - 1 < nj) {
+      W8A8_WAIT_LGKM0();   // the reads of the slot about to be refilled have returned
+      issue(wave + (j + NS - 1) * NW, (j + NS - 1) % NS);
+    }
+    wait_stages<C::kDma>(min(nj - 1 - j, NS - 1));
+    const int8_t* bp = ring + (j % NS) * SB;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      v4i a[RW], b[MT];
+#pragma unroll
+      for (int rw = 0; rw < RW; ++rw) a[rw] = *reinterpret_cast<const v4i*>(bp + rw * 16 * BK + foff[h]);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        b[mt] = *reinterpret_cast<const v4i*>(bp + C::kWBytes + mt * 16 * BK + foff[h]);
+#pragma unroll
+      for (int rw = 0; rw < RW; ++rw)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          acc[rw][mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[rw], b[mt], acc[rw][mt], 0, 0, 0);
+    }
+  }
+
+  // Sum the NW partial tiles (stage buffers reused once every wave is done);
+  // tile t = rw * MT + mt is finished by wave t % NW, whose lane l then holds
+  // token 16 mt + l % 16 and channels 16 rw + 4 (l / 16) + e.
+  __syncthreads();
+  v4i* red = reinterpret_cast<v4i*>(lds);
+#pragma unroll
+  for (int rw = 0; rw < RW; ++rw)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) red[(wave * RW * MT + rw * MT + mt) * kWave + lane] = acc[rw][mt];
+  __syncthreads();
+#pragma unroll
+  for (int rw = 0; rw < RW; ++rw)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int t = rw * MT + mt;
+      if (t % NW != wave) continue;
+      v4i sum = red[t * kWave + lane];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) sum += red[(w * RW * MT + t) * kWave + lane];
+      const int m = mt * 16 + r;
+      const int n = n0 + 16 * rw + 4 * g;
+      if (m < M && n < N) {
+        const float stm = I32OUT ? 0.0f : st[mt];
+        store4<I32OUT>(y, ldy, c, ldc, m, n, N, vec_out, stm, sc[rw], sum[0], sum[1], sum[2],
+                       sum[3]);
+      }
+    }
+}
+
 // Compute units of the current device.
 static int device_cus() {
   int dev = 0, cus = 0;
@@ -865,12 +980,49 @@ static void launch_skinny(const int8_t* xq, int64_t ldq, const float* s_tok, con
                      s_tok, wq, ldw, s_chan, M, N, K, y, ldy, c, ldc, vec_out);
 }
 
+template <int MT, int RW, int NW, int NS, bool I32OUT>
+static void launch_mid(const int8_t* xq, int64_t ldq, const float* s_tok, const int8_t* wq,
+                       int64_t ldw, const float* s_chan, int M, int N, int K, uint16_t* y,
+                       int64_t ldy, int32_t* c, int64_t ldc, bool vec_out, hipStream_t s) {
+  const dim3 grid((unsigned)((N + 16 * RW - 1) / (16 * RW))), block(NW * kWave);
+  hipLaunchKernelGGL((gemm_mid_kernel<MT, RW, NW, NS, I32OUT>), grid, block, 0, s, xq, ldq, s_tok,
+                     wq, ldw, s_chan, M, N, K, y, ldy, c, ldc, vec_out);
+}
+
 template <bool I32OUT>
 static hipError_t launch_gemm_t(const int8_t* xq, int64_t ldq, const float* s_tok,
                                 const int8_t* wq, int64_t ldw, const float* s_chan, int M,
                                 int N, int K, uint16_t* y, int64_t ldy, int32_t* c, int64_t ldc,
                                 bool vec_out, hipStream_t s) {
-  if (M <= kSkinnyMaxM) {
+  if (M <= kSkinnyMaxM && K % MidCfg<1, 1, 1, 2>::kBK == 0) {
+#define W8A8_MID(MTV, RWV, NWV, NSV)                                                          \
+  launch_mid<MTV, RWV, NWV, NSV, I32OUT>(xq, ldq, s_tok, wq, ldw, s_chan, M, N, K, y, ldy, c, ldc, \
+                                         vec_out, s)
+    // Shape classes measured on MI355X (Llama-3.1-8B projection shapes):
+    // wide N takes 64 channels per workgroup once there are enough tokens to
+    // reuse each weight fragment, mid N 32; otherwise 16 channels, so that
+    // N = 4096 still gives one workgroup per CU.
+    const bool wide = N >= 16384, mid = N > 4096 && !wide, deep = K > 8192;
+    if (M <= 16) {
+      if (mid) W8A8_MID(1, 2, 8, 3);
+      else if (wide || deep) W8A8_MID(1, 1, 4, 3);
+      else W8A8_MID(1, 1, 8, 4);
+    } else if (M <= 32) {
+      if (wide) W8A8_MID(2, 4, 4, 3);
+      else if (mid) W8A8_MID(2, 2, 4, 4);
+      else if (deep) W8A8_MID(2, 1, 4, 4);
+      else W8A8_MID(2, 1, 8, 3);
+    } else if (M <= 48) {
+      if (wide) W8A8_MID(3, 4, 2, 3);
+      else if (mid) W8A8_MID(3, 2, 4, 3);
+      else W8A8_MID(3, 1, 4, 3);
+    } else {
+      if (wide) W8A8_MID(4, 4, 2, 2);
+      else if (mid) W8A8_MID(4, 2, 4, 3);
+      else W8A8_MID(4, 1, 4, 3);
+    }
+#undef W8A8_MID
+  } else if (M <= kSkinnyMaxM) {
 #define W8A8_SKINNY(MTV, RWV, NWV, UV, LATEV)                                            \
   launch_skinny<MTV, RWV, NWV, UV, I32OUT, LATEV>(xq, ldq, s_tok, wq, ldw, s_chan, M, N, K, y, \
                                                   ldy, c, ldc, vec_out, s)

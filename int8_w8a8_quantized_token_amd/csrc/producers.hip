@@ -90,30 +90,9 @@ __device__ __forceinline__ float block_max_f(float v, float* red) {
 }
 
 // Codes of 8 values of one row (as in the per-token quantizer).
-__device__ __forceinline__ void codes8(int8_t* __restrict__ qr, int vi, const float (&v)[8],
-                                       float S, float R, bool fast) {
-  int c[8];
-  if (S == 0.0f) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) c[e] = 0;
-  } else {
-    uint32_t slow = fast ? 0u : 0xFFu;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      bool ok;
-      c[e] = (int)code_fast(v[e], R, ok);
-      slow |= ok ? 0u : (1u << e);
-    }
-    if (slow != 0u) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (slow & (1u << e)) c[e] = int8_code(v[e] / S);
-    }
-  }
-  uint2 packed;
-  packed.x = pack4_i8(c[0], c[1], c[2], c[3]);
-  packed.y = pack4_i8(c[4], c[5], c[6], c[7]);
-  *reinterpret_cast<uint2*>(qr + (int64_t)vi * 8) = packed;
+__device__ __forceinline__ void store_codes8(int8_t* __restrict__ qr, int vi, const float (&v)[8],
+                                             float S, float R, bool fast) {
+  *reinterpret_cast<uint2*>(qr + (int64_t)vi * 8) = codes8(v, S, R, fast);
 }
 
 __device__ __forceinline__ void unpack8(uint4 raw, float (&v)[8]) {
@@ -196,7 +175,7 @@ __global__ __launch_bounds__(BS) void rmsnorm_quantize_kernel(
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int vi = tid + i * BS;
-    if (vi < nvec) codes8(q + row * ldq, vi, v[i], S, R, fast);
+    if (vi < nvec) store_codes8(q + row * ldq, vi, v[i], S, R, fast);
   }
 }
 
@@ -242,7 +221,7 @@ __global__ __launch_bounds__(BS) void silu_mul_quantize_kernel(
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int vi = tid + i * BS;
-    if (vi < nvec) codes8(q + row * ldq, vi, v[i], S, R, fast);
+    if (vi < nvec) store_codes8(q + row * ldq, vi, v[i], S, R, fast);
   }
 }
 

@@ -55,33 +55,10 @@ __device__ __forceinline__ void load_prep8(const uint16_t* __restrict__ xr,
   }
 }
 
-// Codes of 8 values under one row scale, stored as 8 bytes. R = RN(1 / scale)
-// and fast = code_fast_ok(scale); values the fast form leaves open (and all
-// of them when fast is false) are divided. A scale of 0 gives code 0.
+// Codes of 8 values under one row scale, stored as 8 bytes.
 __device__ __forceinline__ void store_codes8(int8_t* __restrict__ qr, int vi, const float (&v)[8],
                                              float scale, float R, bool fast) {
-  int c[8];
-  if (scale == 0.0f) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) c[e] = 0;
-  } else {
-    uint32_t slow = fast ? 0u : 0xFFu;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      bool ok;
-      c[e] = (int)code_fast(v[e], R, ok);
-      slow |= ok ? 0u : (1u << e);
-    }
-    if (slow != 0u) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (slow & (1u << e)) c[e] = int8_code(v[e] / scale);
-    }
-  }
-  uint2 packed;
-  packed.x = pack4_i8(c[0], c[1], c[2], c[3]);
-  packed.y = pack4_i8(c[4], c[5], c[6], c[7]);
-  *reinterpret_cast<uint2*>(qr + (int64_t)vi * 8) = packed;
+  *reinterpret_cast<uint2*>(qr + (int64_t)vi * 8) = codes8(v, scale, R, fast);
 }
 
 // Block-wide max of nonnegative values; every thread gets the result.

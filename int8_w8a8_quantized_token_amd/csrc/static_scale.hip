@@ -61,28 +61,7 @@ __global__ __launch_bounds__(kStaticThreads) void quantize_static_kernel(
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] = v[e] / sv[e];
     }
-    int c[8];
-    if (S == 0.0f) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) c[e] = 0;
-    } else {
-      uint32_t slow = fast ? 0u : 0xFFu;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        bool ok;
-        c[e] = (int)code_fast(v[e], R, ok);
-        slow |= ok ? 0u : (1u << e);
-      }
-      if (slow != 0u) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (slow & (1u << e)) c[e] = int8_code(v[e] / S);
-      }
-    }
-    uint2 packed;
-    packed.x = pack4_i8(c[0], c[1], c[2], c[3]);
-    packed.y = pack4_i8(c[4], c[5], c[6], c[7]);
-    *reinterpret_cast<uint2*>(q + r * ldq + (int64_t)vi * 8) = packed;
+    *reinterpret_cast<uint2*>(q + r * ldq + (int64_t)vi * 8) = codes8(v, S, R, fast);
   }
 }
 

@@ -154,6 +154,12 @@ GEMM_SHAPES = [
     (48, 64, 4096), (64, 4096, 4096), (5, 6144, 14336 + 16),
     # skinny classes that load the epilogue scales after the weight stream
     (12, 6000, 1024), (20, 9000, 256), (64, 8320, 512),
+    # LDS-staged decode path (M <= 64, K % 128 == 0): every token class x
+    # (wide, mid, deep, plain N), N ragged against 16/32/64-channel
+    # workgroups, one K stage (fewer stages than waves) and odd stage counts
+    (1, 16400, 128), (3, 5000, 8320), (7, 4100, 256), (16, 300, 384), (17, 16400, 1024),
+    (24, 4500, 128), (31, 1000, 8320), (33, 16390, 512), (40, 6000, 256), (47, 200, 128),
+    (49, 17000, 384), (55, 4200, 1152), (63, 100, 8320), (64, 16, 128),
     # tiled path
     (65, 1, 16), (65, 128, 64), (100, 129, 112), (128, 256, 4096), (130, 300, 1040),
     (257, 515, 208), (512, 512, 2048), (1000, 384, 4096 + 48),
