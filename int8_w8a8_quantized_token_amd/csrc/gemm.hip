@@ -11,13 +11,16 @@
 // quantization is hard, and how SmoothQuant fixes it"). Both operands are
 // K-contiguous ("NT"), as the quantizers write them.
 //
-// Two kernels:
-//   * skinny (M <= 64, decode): the weight matrix is streamed once from HBM
-//     directly into MFMA operand registers; a workgroup owns 16 output
-//     channels and its waves split K; partial int32 tiles are summed in LDS.
-//     v_mfma_i32_16x16x64_i8: the weight rows are the A operand, the token
-//     rows the B operand.
-//   * tiled (prefill): LDS-staged, double-buffered tiles with
+// Kernels:
+//   * mid (M <= 64, decode, K % 128 == 0): the weight matrix is streamed
+//     once from HBM; a workgroup owns 16*RW output channels and all token
+//     rows, its waves split K, and each wave feeds its own ring of LDS
+//     stages by direct global -> LDS loads of whole lines; partial int32
+//     tiles are summed in LDS. v_mfma_i32_16x16x64_i8: the weight rows are
+//     the A operand, the token rows the B operand.
+//   * skinny (M <= 64, other K): the same work split, operands loaded
+//     straight into MFMA registers.
+//   * prefill (M >= 512) and tiled (64 < M < 512): LDS-staged tiles with
 //     v_mfma_i32_32x32x32_i8.
 //
 // MFMA operand layout: for both operands lane l supplies row (l % R) of its
