@@ -122,13 +122,17 @@ size_t w8a8_linear_workspace_bytes(int64_t M, int64_t K);
 /*
  * The whole linear: w8a8_quantize_act into the workspace, then w8a8_gemm,
  * in stream order. One quantize-dequantize cycle per call, as part 2,
- * "Inter-token latency (ITL)" counts them per layer and request.
+ * "Inter-token latency (ITL)" counts them per layer and request. For
+ * M <= 2, N < 16384, K % 128 == 0 and K <= 4096 both steps run in one
+ * kernel launch (every workgroup quantizes the rows itself) and the
+ * workspace is not touched; y is the same either way.
  *   x [M, K] bf16, ldx >= K; smooth [K] or NULL         (read)
  *   wq [N, K] int8, ldw >= K; s_chan [N]                (read)
  *   y [M, N] bf16, ldy >= N                             (written)
  *   workspace: device memory of at least
  *              w8a8_linear_workspace_bytes(M, K) bytes, 256-byte aligned;
- *              overwritten; must not be shared by calls that may overlap.
+ *              contents afterwards unspecified; must not be shared by
+ *              calls that may overlap.
  */
 w8a8_status_t w8a8_linear(const uint16_t* x, int64_t ldx, const float* smooth,
                           const int8_t* wq, int64_t ldw, const float* s_chan,
@@ -210,7 +214,8 @@ w8a8_status_t w8a8_quantize_act_static(const uint16_t* x, int64_t ldx, const flo
 
 /*
  * w8a8_linear with the static scale: w8a8_quantize_act_static into the
- * workspace (same layout and size as w8a8_linear's), then w8a8_gemm.
+ * workspace (same layout and size as w8a8_linear's), then w8a8_gemm; in one
+ * launch under the same conditions as w8a8_linear's.
  */
 w8a8_status_t w8a8_linear_static(const uint16_t* x, int64_t ldx, const float* smooth,
                                  const float* scale, const int8_t* wq, int64_t ldw,

@@ -9,7 +9,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libw8a8.so")
-SOURCES = ["api.hip", "quantize.hip", "gemm.hip", "static_scale.hip", "producers.hip", "gptq.hip"]
+SOURCES = ["api.hip", "quantize.hip", "gemm.hip", "static_scale.hip", "producers.hip", "gptq.hip", "linear_fused.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-mcode-object-version=5", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -141,6 +141,11 @@ w8a8_status_t w8a8_linear(const uint16_t* x, int64_t ldx, const float* smooth, c
     return W8A8_ERROR_WORKSPACE;
   if (!aligned(workspace, 256)) return W8A8_ERROR_MISALIGNED;
 
+  // One or two tokens on a short, narrow weight: one launch that quantizes
+  // inside the GEMM (same codes and scales).
+  if (w8a8::linear_fused_supported(M, N, K))
+    return from_hip(w8a8::launch_linear_fused(x, ldx, smooth, wq, ldw, s_chan, M, N, K, y, ldy,
+                                              stream));
   int8_t* xq = static_cast<int8_t*>(workspace);
   float* s_tok = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256((size_t)M * K));
   W8A8_TRY(from_hip(w8a8::launch_quantize_rows(w8a8::RowMode::kActivation, x, ldx, smooth, M, K,
@@ -179,6 +184,9 @@ w8a8_status_t w8a8_linear_static(const uint16_t* x, int64_t ldx, const float* sm
     return W8A8_ERROR_WORKSPACE;
   if (!aligned(workspace, 256)) return W8A8_ERROR_MISALIGNED;
 
+  if (w8a8::linear_fused_supported(M, N, K))
+    return from_hip(w8a8::launch_linear_fused_static(x, ldx, smooth, scale, wq, ldw, s_chan, M, N,
+                                                     K, y, ldy, stream));
   int8_t* xq = static_cast<int8_t*>(workspace);
   float* s_tok = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256((size_t)M * K));
   W8A8_TRY(from_hip(

@@ -339,32 +339,6 @@ constexpr int GROUP_M = 4;                        // M tiles per tile group
 
 __device__ __forceinline__ int lds_swz(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
 
-// s_waitcnt with vmcnt = n and the other counters left alone (gfx9 encoding).
-#define W8A8_WAIT_VM(n) \
-  __builtin_amdgcn_s_waitcnt(((n) & 0xF) | ((((n) >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8))
-
-// s_waitcnt lgkmcnt(0) with the other counters left alone.
-#define W8A8_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt((0xF) | (3 << 14) | (0x7 << 4))
-
-__device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::: "memory"); }
-
-// One global_load_lds_dwordx4: each lane's 16 bytes at gptr land in LDS at
-// lds_base + 16 * lane (lds_base is wave-uniform). Issued as inline asm so
-// that the compiler's wait-count pass does not treat it as a pending LDS
-// write (it would otherwise drain every outstanding DMA before the next LDS
-// read); the kernel's explicit vmcnt waits order it instead. No output
-// registers; the address is read at issue.
-__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(gptr), "s"(__builtin_amdgcn_readfirstlane(lds_base))
-               : "memory", "m0");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void*)p);
-}
-
 // WN x WM waves; wave (wn, wm) owns output channels [wn*TN/WN, +TN/WN) and
 // tokens [wm*TM/WM, +TM/WM) of the tile as FN x FM 32x32 fragments.
 template <int WN, int WM>
@@ -602,7 +576,6 @@ namespace pf128 {
 constexpr int TM = 256, BK = 128, WN = 2, WM = 4, THREADS = WN * WM * kWave;
 }  // namespace pf128
 
-__device__ __forceinline__ int lds_swz8(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
 template <int TNV>
 struct Prefill128Cfg {
@@ -788,17 +761,6 @@ struct MidCfg {
   static_assert(kLdsBytes <= 160 * 1024, "LDS");
   static_assert(NW * RW * MT * kWave * 16 <= kLdsBytes, "partial tiles fit in the stage buffers");
 };
-
-// Waits until at most n * per DMA instructions of this wave are outstanding
-// (n < 4; s_waitcnt takes an immediate).
-template <int PER>
-__device__ __forceinline__ void wait_stages(int n) {
-  if (n >= 3) W8A8_WAIT_VM(3 * PER);
-  else if (n == 2) W8A8_WAIT_VM(2 * PER);
-  else if (n == 1) W8A8_WAIT_VM(PER);
-  else W8A8_WAIT_VM(0);
-  asm volatile("" ::: "memory");     // LDS reads stay below the wait
-}
 
 template <int MT, int RW, int NW, int NS, bool I32OUT>
 __global__ __launch_bounds__(NW * kWave) void gemm_mid_kernel(

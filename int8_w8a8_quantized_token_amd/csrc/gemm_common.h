@@ -54,4 +54,52 @@ __device__ __forceinline__ void load_chan4(const float* __restrict__ s_chan, int
   for (int e = 0; e < 4; ++e) sc[e] = s_chan[min(n + e, N - 1)];
 }
 
+
+// ---------------------------------------------------------------------------
+// Direct global -> LDS loads and their waits.
+// ---------------------------------------------------------------------------
+
+// s_waitcnt with vmcnt = n and the other counters left alone (gfx9 encoding).
+#define W8A8_WAIT_VM(n) \
+  __builtin_amdgcn_s_waitcnt(((n) & 0xF) | ((((n) >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8))
+
+// s_waitcnt lgkmcnt(0) with the other counters left alone.
+#define W8A8_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt((0xF) | (3 << 14) | (0x7 << 4))
+
+__device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::: "memory"); }
+
+// One global_load_lds_dwordx4: each lane's 16 bytes at gptr land in LDS at
+// lds_base + 16 * lane (lds_base is wave-uniform). Issued as inline asm so
+// that the compiler's wait-count pass does not treat it as a pending LDS
+// write (it would otherwise drain every outstanding DMA before the next LDS
+// read); the kernel's explicit vmcnt waits order it instead. No output
+// registers; the address is read at issue.
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gptr), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void*)p);
+}
+
+// LDS rows of 128 bytes = 8 chunks of 16: row r's chunk c sits at slot
+// c ^ swz8(r), swz8(r) = (r & 7) ^ ((r >> 3) & 1). The 8 rows one 8-lane group
+// reads, and the 8 even / 8 odd rows of a 16-lane group, land in distinct
+// banks; swz8 depends on the low 4 row bits only.
+__device__ __forceinline__ int lds_swz8(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
+// Waits until at most n * per DMA instructions of this wave are outstanding
+// (n < 4; s_waitcnt takes an immediate).
+template <int PER>
+__device__ __forceinline__ void wait_stages(int n) {
+  if (n >= 3) W8A8_WAIT_VM(3 * PER);
+  else if (n == 2) W8A8_WAIT_VM(2 * PER);
+  else if (n == 1) W8A8_WAIT_VM(PER);
+  else W8A8_WAIT_VM(0);
+  asm volatile("" ::: "memory");     // LDS reads stay below the wait
+}
+
 }  // namespace w8a8

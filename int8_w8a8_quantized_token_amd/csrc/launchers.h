@@ -29,6 +29,22 @@ hipError_t launch_gemm(const int8_t* xq, int64_t ldq, const float* s_tok,
                        uint16_t* y, int64_t ldy, int32_t* acc, int64_t ldc,
                        hipStream_t s);
 
+// The whole linear (quantize, GEMM, epilogue) in one launch for
+// M <= kLinearFusedMaxM tokens, N < kLinearFusedMaxN, K % 128 == 0 and
+// K <= kLinearFusedMaxK (linear_fused.hip); dynamic per-token or one static
+// scale. Same results as quantize + GEMM.
+constexpr int64_t kLinearFusedMaxM = 2;
+constexpr int64_t kLinearFusedMaxN = 16384;
+constexpr int64_t kLinearFusedMaxK = 4096;
+bool linear_fused_supported(int64_t M, int64_t N, int64_t K);
+hipError_t launch_linear_fused(const uint16_t* x, int64_t ldx, const float* smooth,
+                               const int8_t* wq, int64_t ldw, const float* s_chan, int64_t M,
+                               int64_t N, int64_t K, uint16_t* y, int64_t ldy, hipStream_t s);
+hipError_t launch_linear_fused_static(const uint16_t* x, int64_t ldx, const float* smooth,
+                                      const float* scale, const int8_t* wq, int64_t ldw,
+                                      const float* s_chan, int64_t M, int64_t N, int64_t K,
+                                      uint16_t* y, int64_t ldy, hipStream_t s);
+
 // Static per-tensor scale: quantizer and calibration (static_scale.hip).
 hipError_t launch_quantize_static(const uint16_t* x, int64_t ldx, const float* smooth,
                                   const float* scale, int64_t M, int64_t K, int8_t* q,

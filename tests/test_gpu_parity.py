@@ -287,6 +287,35 @@ def test_linear_against_oracle(M, N, K):
     check_bf16(host(y), ref["y64"], ref["y"])
 
 
+# The one-launch linear (M <= 2, N < 16384, K % 128 == 0, K <= 4096): both
+# entry points against the oracle, with and without smoothing, a zero row,
+# one K stage, N ragged against 16- and 32-channel workgroups, and the
+# shapes just outside its range (N = 16384, K = 4224: quantize + GEMM).
+FUSED_SHAPES = [(1, 1, 128), (1, 100, 4096), (1, 4096, 4096), (1, 4100, 256), (1, 16383, 1024),
+                (2, 17, 128), (2, 6144, 4096), (2, 4096, 384), (1, 16384, 4096), (2, 300, 4224)]
+
+
+@pytest.mark.parametrize("M,N,K", FUSED_SHAPES, ids=[f"M{m}_N{n}_K{k}" for m, n, k in FUSED_SHAPES])
+@pytest.mark.parametrize("use_smooth", [False, True], ids=["plain", "smooth"])
+def test_linear_one_launch_against_oracle(M, N, K, use_smooth):
+    x = act(M, K, "fused")
+    if M == 2:
+        x[1] = 0                                   # zero row: S = 0, codes 0, y = 0
+    wq = i8((N, K), "fused-w")
+    sw = (WL.rng("fused-sw", N, K).uniform(0.5, 2.0, N) * 1e-3).astype(F32)
+    smooth = np.exp(WL.rng("fused-s", K).uniform(-2, 2, K)).astype(F32) if use_smooth else None
+    ref = O.linear(x, smooth, wq, sw)
+    S = F32(0.04)
+    ref_st = O.linear_static(x, smooth, S, wq, sw)
+    xd, wqd, swd = dev_bf16(x), dev(wq), dev(sw)
+    sd = dev(smooth) if use_smooth else None
+    y = W.w8a8_linear(xd, sd, wqd, swd)
+    y_st = W.w8a8_linear_static(xd, sd, dev(np.array([S], F32)), wqd, swd)
+    torch().cuda.synchronize()
+    check_bf16(host(y), ref["y64"], ref["y"])
+    check_bf16(host(y_st), ref_st["y64"], ref_st["y"], "y static")
+
+
 def test_linear_single_workload_full():
     """The 16-token 4096x4096 layer, every output compared."""
     wl = WL.WORKLOADS["single"]
