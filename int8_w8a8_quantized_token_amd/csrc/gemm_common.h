@@ -91,6 +91,11 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // banks; swz8 depends on the low 4 row bits only.
 __device__ __forceinline__ int lds_swz8(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
+// Stage rotation of the LDS-staged decode kernels for weight rows a
+// multiple of 4 KB apart: workgroup b starts its K walk at stage
+// (b * kMidRotation) mod (K / 128).
+constexpr int kMidRotation = 9;
+
 // Waits until at most n * per DMA instructions of this wave are outstanding
 // (n < 4; s_waitcnt takes an immediate).
 template <int PER>

@@ -58,7 +58,7 @@ __global__ __launch_bounds__(NW * kWave) void linear_fused_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const float* __restrict__ smooth,
     const float* __restrict__ scale, const int8_t* __restrict__ wq, int64_t ldw,
     const float* __restrict__ s_chan, int M, int N, int K, uint16_t* __restrict__ y, int64_t ldy,
-    bool vec_out) {
+    bool vec_out, int rot) {
   using C = FusedCfg<MQ, KMAX, RW, NW, NS>;
   constexpr int BK = C::kBK, SB = C::kStageBytes, PV = C::kPV, LDK = C::kLdk;
   constexpr int BS = C::kThreads;
@@ -104,15 +104,18 @@ __global__ __launch_bounds__(NW * kWave) void linear_fused_kernel(
     const int p = i * kWave + lane;
     wsrc[i] = wq + (int64_t)min(n0 + (p >> 3), N - 1) * ldw + ((p & 7) ^ lds_swz8(p >> 3)) * 16;
   }
+  // Workgroup b walks K from stage (b * rot) mod nst, as the mid GEMM does.
+  const int nst = K / BK;
+  const int first = (int)((int64_t)blockIdx.x * rot % nst);
+  auto kstage = [&](int stage) { return stage + first < nst ? stage + first : stage + first - nst; };
   int8_t* const ring = ring_lds + wave * NS * SB;
   const uint32_t ring_addr = lds_addr(ring);
   auto issue = [&](int stage, int slot) {
     const uint32_t base = ring_addr + slot * SB;
-    const int64_t k0 = (int64_t)stage * BK;
+    const int64_t k0 = (int64_t)kstage(stage) * BK;
 #pragma unroll
     for (int i = 0; i < C::kDma; ++i) dma16(wsrc[i] + k0, base + i * kWave * 16);
   };
-  const int nst = K / BK;
   const int nj = nst > wave ? (nst - wave + NW - 1) / NW : 0;
 #pragma unroll
   for (int j = 0; j < NS - 1; ++j)
@@ -195,7 +198,7 @@ __global__ __launch_bounds__(NW * kWave) void linear_fused_kernel(
     }
     wait_stages<C::kDma>(min(nj - 1 - j, NS - 1));
     const int8_t* bp = ring + (j % NS) * SB;
-    const int stage = wave + j * NW;
+    const int stage = kstage(wave + j * NW);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const v4i b = *reinterpret_cast<const v4i*>(cp + stage * BK + h * 64);
@@ -235,12 +238,13 @@ static void launch_fused(const uint16_t* x, int64_t ldx, const float* smooth, co
                          const int8_t* wq, int64_t ldw, const float* s_chan, int M, int N, int K,
                          uint16_t* y, int64_t ldy, bool vec, hipStream_t s) {
   const dim3 grid((unsigned)((N + 16 * RW - 1) / (16 * RW))), block(NW * kWave);
+  const int rot = ldw % 4096 == 0 ? kMidRotation : 0;
   if (smooth)
     hipLaunchKernelGGL((linear_fused_kernel<MQ, KMAX, RW, NW, NS, true, STATIC>), grid, block, 0,
-                       s, x, ldx, smooth, scale, wq, ldw, s_chan, M, N, K, y, ldy, vec);
+                       s, x, ldx, smooth, scale, wq, ldw, s_chan, M, N, K, y, ldy, vec, rot);
   else
     hipLaunchKernelGGL((linear_fused_kernel<MQ, KMAX, RW, NW, NS, false, STATIC>), grid, block, 0,
-                       s, x, ldx, smooth, scale, wq, ldw, s_chan, M, N, K, y, ldy, vec);
+                       s, x, ldx, smooth, scale, wq, ldw, s_chan, M, N, K, y, ldy, vec, rot);
 }
 
 bool linear_fused_supported(int64_t M, int64_t N, int64_t K) {
