@@ -11,8 +11,10 @@
 //     new residual stream); ms = sum(h^2) / K rounded once to binary32;
 //     inv = 1 / sqrt(ms + eps); y = (h * inv) * g with g = gamma / s; then
 //     S = max|y| / 127 and codes;
-//   * SiLU-gated product + quantize: m = bf16((g / (1 + exp(-g))) * u) in
-//     binary64 from the bf16 gate and up halves of a row; x' = m / s; codes.
+//   * SiLU-gated product + quantize: m = bf16((g / (1 + exp(-g))) * u), the
+//     real value rounded once (a binary32 evaluation with a proven error
+//     bound where that decides the rounding, binary64 elsewhere), from the
+//     bf16 gate and up halves of a row; x' = m / s; codes.
 //
 // The sum of squares is exact per term (a bf16 square fits binary64) and is
 // accumulated with error-free transformations (two-sum, double-double), so
@@ -183,6 +185,51 @@ __global__ __launch_bounds__(BS) void rmsnorm_quantize_kernel(
 // SiLU-gated product + quantize
 // ---------------------------------------------------------------------------
 
+// e^x for |x| <= 80 in binary32: x = n ln 2 + r with a two-part ln 2 (fused
+// multiply-adds), e^r by its Taylor polynomial to degree 7 (|r| <= ln2 / 2,
+// remainder below 2^-26.5 relative), then the exact scaling by 2^n. Relative
+// error below 3 * 2^-24.
+__device__ __forceinline__ float exp_bounded(float x) {
+  const float n = __builtin_rintf(x * 0x1.715476p+0f);   // log2(e)
+  float r = fmaf(-n, 0x1.62e43p-1f, x);                  // ln 2, high part
+  r = fmaf(-n, -0x1.05c61p-29f, r);                      // ln 2, low part
+  float p = 0x1.a01a02p-13f;                             // 1/7!
+  p = fmaf(p, r, 0x1.6c16c2p-10f);                       // 1/6!
+  p = fmaf(p, r, 0x1.111112p-7f);                        // 1/5!
+  p = fmaf(p, r, 0x1.555556p-5f);                        // 1/4!
+  p = fmaf(p, r, 0x1.555556p-3f);                        // 1/3!
+  p = fmaf(p, r, 0.5f);
+  p = fmaf(p, r, 1.0f);
+  p = fmaf(p, r, 1.0f);
+  return ldexpf(p, (int)n);
+}
+
+// bf16(g / (1 + e^-g) * u) from a binary32 evaluation, when that is certain.
+// For |g| <= 80 the binary32 value is within 7 ulps of the real one (exp
+// 3 * 2^-24, then 1 + e, the division and the product one rounding each), so
+// its bf16 rounding is the real value's whenever its low 16 bits are more
+// than 16 away from 0x8000, the rounding boundary, and it is a normal number
+// of moderate size; a zero gate or up value gives an exact zero. ok = false
+// for everything else. tests/exhaustive/silu_fastpath_check.c runs this
+// decision for every pair of finite bf16 inputs.
+__device__ __forceinline__ float silu_mul_fast(float g, float u, bool& ok) {
+  const float q = g / (1.0f + exp_bounded(-g));
+  const float m = q * u;
+  const float a = fabsf(m);
+  const int lo = (int)(__float_as_uint(m) & 0xFFFFu);
+  const bool clear = lo > 0x8000 + 16 || lo < 0x8000 - 16;
+  ok = fabsf(g) <= 80.0f &&
+       (g == 0.0f || u == 0.0f || (a >= 0x1p-120f && a < 0x1p120f && clear));
+  return __uint_as_float(f32_to_bf16_rne(m) << 16);
+}
+
+// The same value evaluated in binary64 and rounded once to bf16.
+__device__ __forceinline__ float silu_mul_f64(float g, float u) {
+  const double gd = (double)g;
+  const double m = (gd / (1.0 + exp(-gd))) * (double)u;
+  return __uint_as_float((uint32_t)f64_to_bf16_rne(m) << 16);
+}
+
 template <int BS, int NV, bool SMOOTH>
 __global__ __launch_bounds__(BS) void silu_mul_quantize_kernel(
     const uint16_t* __restrict__ gu, int64_t ldgu, const float* __restrict__ smooth, int I,
@@ -202,11 +249,31 @@ __global__ __launch_bounds__(BS) void silu_mul_quantize_kernel(
       float gv[8], uv[8];
       unpack8(*reinterpret_cast<const uint4*>(gr + (int64_t)vi * 8), gv);
       unpack8(*reinterpret_cast<const uint4*>(gr + I + (int64_t)vi * 8), uv);
+      float mv[8];
+      uint32_t slow = 0u;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const double gd = (double)gv[e];
-        const double m = (gd / (1.0 + exp(-gd))) * (double)uv[e];
-        float mf = __uint_as_float((uint32_t)f64_to_bf16_rne(m) << 16);
+        bool ok;
+        mv[e] = silu_mul_fast(gv[e], uv[e], ok);
+        slow |= ok ? 0u : (1u << e);
+      }
+      // The undecided values in binary64, one per lane per pass, so that a
+      // wave runs the slow path about once however its lanes' values fall.
+      while (slow != 0u) {
+        const int idx = __builtin_ctz(slow);
+        float gs = gv[0], us = uv[0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e)
+          if (idx == e) { gs = gv[e]; us = uv[e]; }
+        const float r = silu_mul_f64(gs, us);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (idx == e) mv[e] = r;
+        slow &= slow - 1u;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float mf = mv[e];
         if constexpr (SMOOTH) mf = mf / smooth[vi * 8 + e];
         v[i][e] = mf;
         amax = fmaxf(amax, fabsf(mf));
