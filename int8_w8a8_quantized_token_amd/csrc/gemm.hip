@@ -732,9 +732,10 @@ __global__ __launch_bounds__(pf128::THREADS, 1) void gemm_prefill128_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Mid kernel (decode batches of 17..64 tokens, K % 128 == 0). The skinny
-// kernel's split of the work: a workgroup owns 16*RW output channels and all
-// 16*MT token rows, its NW waves take interleaved K stages of 128 bytes and
+// Mid kernel (decode batches up to a few hundred tokens, K % 128 == 0). The
+// skinny kernel's split of the work: a workgroup owns 16*RW output channels
+// and 16*MT token rows (M tile blockIdx.y), its NW waves take interleaved K
+// stages of 128 bytes and
 // sum their partial tiles in LDS at the end. But each wave brings its
 // operands in through LDS with direct global -> LDS loads of whole 128-byte
 // lines (the token tile is most of the bytes once M > 16, and register
@@ -782,12 +783,12 @@ __global__ __launch_bounds__(NW * kWave) void gemm_mid_kernel(
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int r = lane & 15, g = lane >> 4;
-  const int n0 = blockIdx.x * 16 * RW;
+  const int n0 = blockIdx.x * 16 * RW, m0 = blockIdx.y * 16 * MT;
 
   float st[MT], sc[RW][4];
   if constexpr (!I32OUT) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) st[mt] = s_tok[min(mt * 16 + r, M - 1)];
+    for (int mt = 0; mt < MT; ++mt) st[mt] = s_tok[min(m0 + mt * 16 + r, M - 1)];
 #pragma unroll
     for (int rw = 0; rw < RW; ++rw) load_chan4(s_chan, n0 + 16 * rw + 4 * g, N, sc[rw]);
   }
@@ -805,7 +806,7 @@ __global__ __launch_bounds__(NW * kWave) void gemm_mid_kernel(
 #pragma unroll
   for (int i = 0; i < DX; ++i) {
     const int p = i * kWave + lane;
-    xsrc[i] = xq + (int64_t)min(p >> 3, M - 1) * ldq + ((p & 7) ^ lds_swz8(p >> 3)) * 16;
+    xsrc[i] = xq + (int64_t)min(m0 + (p >> 3), M - 1) * ldq + ((p & 7) ^ lds_swz8(p >> 3)) * 16;
   }
   const int nst = K / BK;
   const int first = (int)((int64_t)blockIdx.x * rot % nst);
@@ -878,7 +879,7 @@ __global__ __launch_bounds__(NW * kWave) void gemm_mid_kernel(
       v4i sum = red[t * kWave + lane];
 #pragma unroll
       for (int w = 1; w < NW; ++w) sum += red[(w * RW * MT + t) * kWave + lane];
-      const int m = mt * 16 + r;
+      const int m = m0 + mt * 16 + r;
       const int n = n0 + 16 * rw + 4 * g;
       if (m < M && n < N) {
         const float stm = I32OUT ? 0.0f : st[mt];
@@ -958,10 +959,23 @@ template <int MT, int RW, int NW, int NS, bool I32OUT>
 static void launch_mid(const int8_t* xq, int64_t ldq, const float* s_tok, const int8_t* wq,
                        int64_t ldw, const float* s_chan, int M, int N, int K, uint16_t* y,
                        int64_t ldy, int32_t* c, int64_t ldc, bool vec_out, hipStream_t s) {
-  const dim3 grid((unsigned)((N + 16 * RW - 1) / (16 * RW))), block(NW * kWave);
+  const dim3 grid((unsigned)((N + 16 * RW - 1) / (16 * RW)), (unsigned)((M + 16 * MT - 1) / (16 * MT))),
+      block(NW * kWave);
   const int rot = ldw % 4096 == 0 ? kMidRotation : 0;
   hipLaunchKernelGGL((gemm_mid_kernel<MT, RW, NW, NS, I32OUT>), grid, block, 0, s, xq, ldq, s_tok,
                      wq, ldw, s_chan, M, N, K, y, ldy, c, ldc, vec_out, rot);
+}
+
+// Which M take the mid kernel (K % 128 == 0): every decode M, and beyond
+// that while M tiles of 64 rows beat the prefill kernel's 256-row tiles,
+// which fill the 256 CUs only once there are enough of them (measured on
+// MI355X, Llama-3.1-8B shapes: up to M = 128 for 28672 channels, 1536 for
+// K = 14336, 1024 otherwise).
+static bool mid_path(int M, int N, int K) {
+  if (K % MidCfg<1, 1, 1, 2>::kBK != 0) return false;
+  if (M <= kSkinnyMaxM) return true;
+  if (N >= 16384) return M <= 128;
+  return M <= (K > 8192 ? 1536 : 1024);
 }
 
 template <bool I32OUT>
@@ -969,7 +983,7 @@ static hipError_t launch_gemm_t(const int8_t* xq, int64_t ldq, const float* s_to
                                 const int8_t* wq, int64_t ldw, const float* s_chan, int M,
                                 int N, int K, uint16_t* y, int64_t ldy, int32_t* c, int64_t ldc,
                                 bool vec_out, hipStream_t s) {
-  if (M <= kSkinnyMaxM && K % MidCfg<1, 1, 1, 2>::kBK == 0) {
+  if (mid_path(M, N, K)) {
 #define W8A8_MID(MTV, RWV, NWV, NSV)                                                          \
   launch_mid<MTV, RWV, NWV, NSV, I32OUT>(xq, ldq, s_tok, wq, ldw, s_chan, M, N, K, y, ldy, c, ldc, \
                                          vec_out, s)
@@ -991,10 +1005,18 @@ static hipError_t launch_gemm_t(const int8_t* xq, int64_t ldq, const float* s_to
       if (wide) W8A8_MID(3, 4, 2, 3);
       else if (mid) W8A8_MID(3, 2, 4, 3);
       else W8A8_MID(3, 1, 4, 3);
-    } else {
+    } else if (M <= kSkinnyMaxM) {
       if (wide) W8A8_MID(4, 4, 2, 2);
       else if (mid) W8A8_MID(4, 2, 4, 3);
       else W8A8_MID(4, 1, 4, 3);
+    } else if (M <= 128) {     // several M tiles of 64 rows from here on
+      if (wide) W8A8_MID(4, 4, 2, 2);
+      else if (mid) W8A8_MID(4, 4, 4, 2);
+      else W8A8_MID(4, 2, 4, 3);
+    } else if (M <= 256 || (mid && M <= 512)) {
+      W8A8_MID(4, 4, 4, 2);
+    } else {
+      W8A8_MID(4, 4, 2, 2);
     }
 #undef W8A8_MID
   } else if (M <= kSkinnyMaxM) {
@@ -1031,7 +1053,7 @@ static hipError_t launch_gemm_t(const int8_t* xq, int64_t ldq, const float* s_to
       else W8A8_SKINNY(4, 1, 8, 8, false);
     }
 #undef W8A8_SKINNY
-  } else if (M >= kPrefillMinM && K % pf128::BK == 0) {
+  } else if (K % pf128::BK == 0) {
     launch_prefill128_auto<I32OUT>(xq, ldq, s_tok, wq, ldw, s_chan, M, N, K, y, ldy, c, ldc,
                                    vec_out, s);
   } else if (M >= kPrefillMinM) {

@@ -160,14 +160,24 @@ GEMM_SHAPES = [
     (1, 16400, 128), (3, 5000, 8320), (7, 4100, 256), (16, 300, 384), (17, 16400, 1024),
     (24, 4500, 128), (31, 1000, 8320), (33, 16390, 512), (40, 6000, 256), (47, 200, 128),
     (49, 17000, 384), (55, 4200, 1152), (63, 100, 8320), (64, 16, 128),
-    # tiled path
+    # the same kernel in M tiles of 64 rows (ragged last tile), up to the
+    # limits of its range, and the prefill kernel just past them (at
+    # M < 512 for wide N)
+    (65, 300, 256), (128, 16400, 128), (129, 16400, 256), (200, 5000, 512), (300, 17000, 128),
+    (700, 300, 1152), (1024, 200, 512), (1025, 200, 512), (1536, 60, 8320), (1537, 60, 8320),
+    # tiled path (64 < M < 512, K % 128 != 0; (128, 256, 4096) and
+    # (512, 512, 2048) take the M-tiled mid kernel)
     (65, 1, 16), (65, 128, 64), (100, 129, 112), (128, 256, 4096), (130, 300, 1040),
     (257, 515, 208), (512, 512, 2048), (1000, 384, 4096 + 48),
-    # prefill path (M >= 512): 0..3 full 64-byte stages, K tails, ragged M/N
+    # 64-byte-stage prefill path (M >= 512, K % 128 != 0): 0..3 full stages,
+    # K tails, ragged M/N
     (512, 256, 48), (512, 256, 64), (513, 257, 128), (600, 300, 192), (700, 520, 208),
     (1024, 768, 14336 + 16), (2048, 1000, 1024),
-    # full-line prefill path (K % 128 == 0): 1, 2 and 3 stages, several tiles, ragged M/N
+    # full-line prefill path (K % 128 == 0, past the mid kernel's range): 1, 2
+    # and 3 stages, several tiles, ragged M/N ((512, 512, 128), (777, 300, 256)
+    # and (1024, 1024, 4096) take the mid kernel)
     (512, 512, 128), (777, 300, 256), (1100, 600, 384), (1024, 1024, 4096),
+    (1030, 520, 128), (1040, 260, 384),
     # enough tiles that 256-row tiles win over 192-row ones
     (2048, 8192, 256), (2047, 8190, 256),
 ]
