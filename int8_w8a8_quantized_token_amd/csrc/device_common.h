@@ -100,11 +100,27 @@ __device__ __forceinline__ uint2 codes8(const float (&v)[8], float S, float R, b
   return uint2{pack4_i8(c[0], c[1], c[2], c[3]), pack4_i8(c[4], c[5], c[6], c[7])};
 }
 
-// Max over a wavefront (all 64 lanes end with the result).
+// One DPP move of a binary32 value within rows of 16 lanes (ctrl constant).
+#define W8A8_DPP_F32(x, ctrl) \
+  __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), (ctrl), 0xF, 0xF, false))
+
+// Max over a wavefront; every lane ends with the result. All 64 lanes must be
+// active. Within each row of 16 lanes: max with the neighbour (quad_perm
+// [1,0,3,2]), with the other pair (quad_perm [2,3,0,1]), with the mirrored
+// half row (row_half_mirror) and with the mirrored row (row_mirror); then the
+// four row maxima through scalar reads. No LDS traffic, unlike a butterfly
+// of cross-lane shuffles (ds_bpermute), whose six LDS round trips sat on the
+// critical path of every row reduction.
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
-  return v;
+  v = fmaxf(v, W8A8_DPP_F32(v, 0xB1));
+  v = fmaxf(v, W8A8_DPP_F32(v, 0x4E));
+  v = fmaxf(v, W8A8_DPP_F32(v, 0x141));
+  v = fmaxf(v, W8A8_DPP_F32(v, 0x140));
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 15));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 31));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 47));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
 }  // namespace w8a8
