@@ -252,7 +252,9 @@ bool linear_fused_supported(int64_t M, int64_t N, int64_t K) {
          K <= kLinearFusedMaxK;
 }
 
-// 32 channels per workgroup for N > 4096, else 16 with 16 waves (measured).
+// 32 channels per workgroup for N > 4096, else 16 (measured): with 8 waves
+// for per-token scales (half the partial maxima to combine), 16 for the
+// static scale (no reduction).
 template <bool STATIC>
 static hipError_t launch_fused_t(const uint16_t* x, int64_t ldx, const float* smooth,
                                  const float* scale, const int8_t* wq, int64_t ldw,
@@ -265,12 +267,13 @@ static hipError_t launch_fused_t(const uint16_t* x, int64_t ldx, const float* sm
 #define W8A8_FUSED(MQV, RWV, NWV, NSV)                                                          \
   launch_fused<MQV, KM, RWV, NWV, NSV, STATIC>(x, ldx, smooth, scale, wq, ldw, s_chan, m, n, k, \
                                                y, ldy, vec, s)
+  constexpr int NWN = STATIC ? 16 : 8;
   if (M == 1) {
     if (mid) W8A8_FUSED(1, 2, 8, 3);
-    else W8A8_FUSED(1, 1, 16, 3);
+    else W8A8_FUSED(1, 1, NWN, 3);
   } else {
     if (mid) W8A8_FUSED(2, 2, 8, 3);
-    else W8A8_FUSED(2, 1, 16, 3);
+    else W8A8_FUSED(2, 1, NWN, 3);
   }
 #undef W8A8_FUSED
   return hipGetLastError();
