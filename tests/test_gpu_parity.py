@@ -231,6 +231,63 @@ def test_gemm_strided_output():
     assert np.all(yh[:, N:] == 0), "wrote past the row"
 
 
+# Row strides past K for both operands and an output stride that rules out
+# vector stores, on every kernel route: LDS-staged decode (one and several M
+# tiles; K = 3968 with weight rows 4096 bytes apart, where the K walk is
+# rotated, over 31 stages), register-staged skinny (K % 128 != 0), tiled,
+# and both prefill kernels.
+STRIDED = [(1, 300, 512, 4096), (33, 200, 3968, 4096), (200, 130, 256, 384), (5, 70, 1040, 1104),
+           (100, 90, 208, 272), (1100, 140, 256, 320), (600, 60, 192, 256)]
+
+
+@pytest.mark.parametrize("M,N,K,ldw", STRIDED, ids=[f"M{m}_N{n}_K{k}_ldw{l}" for m, n, k, l in STRIDED])
+def test_gemm_strided_operands(M, N, K, ldw):
+    ldq, ldy = K + 64, N + 3
+    a, b = i8((M, K), "st-a"), i8((N, K), "st-b")
+    r = WL.rng("st-scales", M, N, K)
+    s_tok = np.exp(r.uniform(-12, -2, M)).astype(F32)
+    s_chan = np.exp(r.uniform(-10, -3, N)).astype(F32)
+    t = torch()
+    aq = t.zeros((M, ldq), dtype=t.int8, device="cuda")
+    aq[:, :K] = dev(a)
+    bw = t.zeros((N, ldw), dtype=t.int8, device="cuda")
+    bw[:, :K] = dev(b)
+    yfull = t.zeros((M, ldy), dtype=t.bfloat16, device="cuda")
+    W.w8a8_gemm(aq[:, :K], dev(s_tok), bw[:, :K], dev(s_chan), y=yfull[:, :N])
+    acc = W.w8a8_gemm_i32(aq[:, :K], bw[:, :K])
+    t.cuda.synchronize()
+    acc_ref = O.gemm_i32(a, b)
+    np.testing.assert_array_equal(host(acc), acc_ref)
+    y64, y_ref = O.dequant_epilogue(acc_ref, s_tok, s_chan)
+    yh = host(yfull)
+    check_bf16(yh[:, :N], y64, y_ref)
+    assert np.all(yh[:, N:] == 0), "wrote past the row"
+
+
+@pytest.mark.parametrize("M", [1, 2])
+def test_linear_one_launch_strided(M):
+    # the one-launch linear on a column slice of a wider input, into an
+    # output whose row stride rules out vector stores
+    K, N, ldx, ldy = 1024, 300, 1536, 303
+    big = act(M, ldx, "fused-slice")
+    w = WL.weights(N, K, 0.02, "fused-slice")
+    xs = big[:, :K]
+    s_ref = smooth_for(xs, w)
+    wq_ref, sw_ref = O.prepare_weight(w, s_ref)
+    ref = O.linear(xs, s_ref, wq_ref, sw_ref)
+    t = torch()
+    xd = dev_bf16(big)[:, :K]
+    wd = dev_bf16(w)
+    s = W.w8a8_smoothing_factors(W.w8a8_channel_absmax(xd), W.w8a8_channel_absmax(wd))
+    wq, sw = W.w8a8_quantize_weight(wd, s)
+    yfull = t.zeros((M, ldy), dtype=t.bfloat16, device="cuda")
+    W.w8a8_linear(xd, s, wq, sw, y=yfull[:, :N])
+    t.cuda.synchronize()
+    yh = host(yfull)
+    check_bf16(yh[:, :N], ref["y64"], ref["y"])
+    assert np.all(yh[:, N:] == 0), "wrote past the row"
+
+
 # ---------------------------------------------------------------------------
 # offline prep kernels (bit-exact)
 # ---------------------------------------------------------------------------
