@@ -58,33 +58,35 @@ def log(*a):
 # same run count exactly its own bytes. "decode": mean over the 16 decode
 # (projection, M) GEMMs; "prefill": mean over the 4 GEMMs at M = 4096. The
 # figures belong to the GEMM code with the recorded SHA-256 (taken over the
-# source with comments and blank lines removed) only; for any other code the
-# field is null.
+# GEMM sources and the headers they include, comments and blank lines
+# removed) only; for any other code the field is null.
 MEASURED_TRAFFIC = {
-    "gemm_code_sha256": "38eece46961b294bcab557e8ad3599c0056f73d8cdcd14c86558566c6d413857",
-    "decode": 56294957,
-    "prefill": 427156558,
+    "gemm_code_sha256": "6b81b99e320e2ccb8c981e2ce951bf4af5ef7abfa2345f0435e98b630e58df3c",
+    "decode": 56294214,
+    "prefill": 426575520,
 }
-GEMM_SRC = os.path.join("int8_w8a8_quantized_token_amd", "csrc", "gemm.hip")
+GEMM_SRCS = [os.path.join("int8_w8a8_quantized_token_amd", "csrc", f)
+             for f in ("gemm.hip", "gemm_common.h", "device_common.h")]
 
 
-def code_sha256(path):
-    """SHA-256 of a C++ source without its // comments and blank lines."""
+def code_sha256(paths):
+    """SHA-256 of C++ sources without their // comments and blank lines."""
     import hashlib
     import re
     lines = []
-    with open(path, encoding="utf-8") as f:
-        for line in f.read().split("\n"):
-            line = re.sub(r"//.*$", "", line).rstrip()
-            if line.strip():
-                lines.append(line)
+    for path in paths:
+        with open(path, encoding="utf-8") as f:
+            for line in f.read().split("\n"):
+                line = re.sub(r"//.*$", "", line).rstrip()
+                if line.strip():
+                    lines.append(line)
     return hashlib.sha256("\n".join(lines).encode()).hexdigest()
 
 
 def measured_traffic(root, which):
     if not MEASURED_TRAFFIC:
         return None
-    if code_sha256(os.path.join(root, GEMM_SRC)) != MEASURED_TRAFFIC["gemm_code_sha256"]:
+    if code_sha256([os.path.join(root, p) for p in GEMM_SRCS]) != MEASURED_TRAFFIC["gemm_code_sha256"]:
         return None
     return MEASURED_TRAFFIC[which]
 

@@ -557,10 +557,19 @@ __device__ __forceinline__ void prefill_tile_coords(int t_lin, int tiles_n, int 
 // Prefill kernel, full-line variant (K % 128 == 0): each stage carries 128
 // bytes of K per row, so every DMA request covers whole 128-byte lines
 // (measured on MI355X: 91 GB/s per CU against 54 GB/s for 64-byte
-// half-lines). Two stages: the DMA of stage s + 1 is issued right after the
-// barrier of stage s and lands while stage s is multiplied. Fragment reads
-// are double-buffered in registers: k-step ks + 1's LDS reads are issued
-// before k-step ks's MFMAs.
+// half-lines). Two stages: the DMA of stage s + 1 lands while stage s is
+// multiplied. Fragment reads are double-buffered in registers: k-step
+// ks + 1's LDS reads go out while k-step ks multiplies.
+//
+// Schedule inside a stage. LDS serves both the fragment reads (192 KB per
+// stage per CU) and the DMA writes (64 KB), about 84% of its bandwidth at
+// the full MFMA rate, so bursts stall the matrix cores. Two things spread
+// the load: each k-step's reads are interleaved one-for-one with its MFMAs
+// (scheduling group barriers), and the next stage's DMA goes out in two
+// halves, one right after the barrier and one after k-step 0's MFMAs.
+// Measured on MI355X at M = 4096 against issuing all reads, then all MFMAs,
+// with the whole DMA after the barrier: 4-10% faster on the Llama-3.1-8B
+// projections (gate_up 494 -> 445 us, down 210 -> 199 us).
 //
 // The tile is TNV weight rows (256, or 192 when that packs the CUs better)
 // by 256 token rows; 8 waves in a 2 x 4 grid.
@@ -625,13 +634,16 @@ __global__ __launch_bounds__(pf128::THREADS, 1) void gemm_prefill128_kernel(
     xsrc[i] = xq + (int64_t)min(m0 + (p >> 3), M - 1) * ldq + ((p & 7) ^ lds_swz8(p >> 3)) * 16;
   }
   const uint32_t lds_base = lds_addr(stages) + wave * kWave * 16;
-  auto issue = [&](int stage) {
+  // DMA instructions [q0, q1) of stage `stage`: weight tile first, then tokens
+  auto issue = [&](int stage, int q0, int q1) {
     const uint32_t base = lds_base + (uint32_t)((stage & 1) * SB);
     const int64_t k0 = (int64_t)stage * BK;
 #pragma unroll
-    for (int i = 0; i < DW; ++i) dma16(wsrc[i] + k0, base + i * THREADS * 16);
-#pragma unroll
-    for (int i = 0; i < DX; ++i) dma16(xsrc[i] + k0, base + WB + i * THREADS * 16);
+    for (int q = 0; q < DW + DX; ++q) {
+      if (q < q0 || q >= q1) continue;
+      if (q < DW) dma16(wsrc[q] + k0, base + q * THREADS * 16);
+      else dma16(xsrc[q - DW] + k0, base + WB + (q - DW) * THREADS * 16);
+    }
   };
 
   // scales for the epilogue, fetched before the K loop
@@ -672,27 +684,39 @@ __global__ __launch_bounds__(pf128::THREADS, 1) void gemm_prefill128_kernel(
   };
 
   const int nst = K / BK;
-  issue(0);
+  issue(0, 0, DW + DX);
   for (int s = 0; s < nst; ++s) {
     W8A8_WAIT_VM(0);                 // this wave's DMA of stage s has landed
     barrier_no_fence();              // everyone's has; stage s - 1 is fully read
-    if (s + 1 < nst) issue(s + 1);
+    const bool more = s + 1 < nst;
+    if (more) issue(s + 1, 0, (DW + DX) / 2);
     const int8_t* bufp = stages + (s & 1) * SB;
     read_frags(bufp, 0, fa[0], fb[0]);
-    // The scheduling fences keep each k-step's reads as one block issued
-    // ahead of the previous k-step's MFMAs (left alone, the scheduler
-    // reuses one fragment register and waits on LDS every two MFMAs).
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       __builtin_amdgcn_sched_barrier(0);
       if (ks < 3) read_frags(bufp, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
-      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < FN; ++i)
 #pragma unroll
         for (int j = 0; j < FM; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[ks & 1][i], fb[ks & 1][j], acc[i][j],
                                                             0, 0, 0);
+      // one MFMA, one LDS read, ..., then the remaining MFMAs
+      if (ks < 3) {
+#pragma unroll
+        for (int q = 0; q < FN + FM; ++q) {
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, FN * FM - FN - FM, 0);
+      } else {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, FN * FM, 0);
+      }
+      if (ks == 0 && more) {
+        __builtin_amdgcn_sched_barrier(0);
+        issue(s + 1, (DW + DX) / 2, DW + DX);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
   }

@@ -68,6 +68,10 @@ __device__ __forceinline__ void load_chan4(const float* __restrict__ s_chan, int
 
 __device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::: "memory"); }
 
+// Instruction classes of __builtin_amdgcn_sched_group_barrier's mask.
+constexpr int kSchedMfma = 0x008;     // MFMA / WMMA
+constexpr int kSchedDsRead = 0x100;   // LDS reads
+
 // One global_load_lds_dwordx4: each lane's 16 bytes at gptr land in LDS at
 // lds_base + 16 * lane (lds_base is wave-uniform). Issued as inline asm so
 // that the compiler's wait-count pass does not treat it as a pending LDS
