@@ -571,8 +571,9 @@ __device__ __forceinline__ void prefill_tile_coords(int t_lin, int tiles_n, int 
 // with the whole DMA after the barrier: 4-10% faster on the Llama-3.1-8B
 // projections (gate_up 494 -> 445 us, down 210 -> 199 us).
 //
-// The tile is TNV weight rows (256, or 192 when that packs the CUs better)
-// by 256 token rows; 8 waves in a 2 x 4 grid.
+// The tile is TNV weight rows by TMV token rows with 8 waves: 256 x 256
+// (waves 2 x 4), 192 x 256 (2 x 4) or 256 x 192 (4 x 2); the choice is
+// launch_prefill128_auto's.
 //
 // LDS row = 128 B = 8 chunks; row r's chunk c sits at slot
 // c ^ swz8(r), swz8(r) = (r & 7) ^ ((r >> 3) & 1): the 8 rows one 8-lane
@@ -582,30 +583,37 @@ __device__ __forceinline__ void prefill_tile_coords(int t_lin, int tiles_n, int 
 // ---------------------------------------------------------------------------
 
 namespace pf128 {
-constexpr int TM = 256, BK = 128, WN = 2, WM = 4, THREADS = WN * WM * kWave;
+constexpr int BK = 128, THREADS = 8 * kWave;
 }  // namespace pf128
 
-
-template <int TNV>
+// TNV weight rows x TMV token rows per workgroup, 8 waves in a WNV x WMV grid,
+// each wave owning FN x FM 32x32 output fragments.
+template <int TNV, int TMV, int WNV, int WMV>
 struct Prefill128Cfg {
-  static constexpr int kTN = TNV;
-  static constexpr int kWBytes = TNV * pf128::BK, kXBytes = pf128::TM * pf128::BK;
+  static constexpr int kWBytes = TNV * pf128::BK, kXBytes = TMV * pf128::BK;
   static constexpr int kStageBytes = kWBytes + kXBytes;
-  static constexpr int kFN = TNV / pf128::WN / 32, kFM = pf128::TM / pf128::WM / 32;
+  static constexpr int kFN = TNV / WNV / 32, kFM = TMV / WMV / 32;
   static constexpr int kDmaW = kWBytes / (pf128::THREADS * 16);
   static constexpr int kDmaX = kXBytes / (pf128::THREADS * 16);
-  static constexpr int kScales = TNV + pf128::TM;
-  static_assert(kDmaW * pf128::THREADS * 16 == kWBytes && kFN * pf128::WN * 32 == TNV, "");
+  static constexpr int kScales = TNV + TMV;
+  static_assert(WNV * WMV * kWave == pf128::THREADS, "8 waves");
+  static_assert(kFN * WNV * 32 == TNV && kFM * WMV * 32 == TMV, "whole fragments per wave");
+  static_assert(kDmaW * pf128::THREADS * 16 == kWBytes && kDmaX * pf128::THREADS * 16 == kXBytes,
+                "whole DMA instructions per operand tile");
+  static_assert(kFN * kFM >= kFN + kFM, "one MFMA per fragment read in the interleaved schedule");
+  static_assert(2 * kStageBytes + 4 * kScales <= 160 * 1024, "LDS");
 };
 
-template <int TNV, bool I32OUT>
+template <int TNV, int TMV, int WNV, int WMV, bool I32OUT>
 __global__ __launch_bounds__(pf128::THREADS, 1) void gemm_prefill128_kernel(
     const int8_t* __restrict__ xq, int64_t ldq, const float* __restrict__ s_tok,
     const int8_t* __restrict__ wq, int64_t ldw, const float* __restrict__ s_chan, int M, int N,
     int K, uint16_t* __restrict__ y, int64_t ldy, int32_t* __restrict__ c, int64_t ldc,
     bool vec_out) {
-  using namespace pf128;
-  using C = Prefill128Cfg<TNV>;
+  using pf128::BK;
+  using pf128::THREADS;
+  using C = Prefill128Cfg<TNV, TMV, WNV, WMV>;
+  constexpr int TM = TMV, WN = WNV;
   constexpr int FN = C::kFN, FM = C::kFM, DW = C::kDmaW, DX = C::kDmaX;
   constexpr int SB = C::kStageBytes, WB = C::kWBytes;
   __shared__ __attribute__((aligned(1024))) int8_t stages[2 * SB];
@@ -923,33 +931,51 @@ static int device_cus() {
   return cus;
 }
 
-template <int TNV, bool I32OUT>
+template <int TNV, int TMV, int WNV, int WMV, bool I32OUT>
 static void launch_prefill128(const int8_t* xq, int64_t ldq, const float* s_tok, const int8_t* wq,
                               int64_t ldw, const float* s_chan, int M, int N, int K, uint16_t* y,
                               int64_t ldy, int32_t* c, int64_t ldc, bool vec_out, hipStream_t s) {
-  const int tiles = ((N + TNV - 1) / TNV) * ((M + pf128::TM - 1) / pf128::TM);
-  hipLaunchKernelGGL((gemm_prefill128_kernel<TNV, I32OUT>), dim3((unsigned)tiles),
+  const int tiles = ((N + TNV - 1) / TNV) * ((M + TMV - 1) / TMV);
+  hipLaunchKernelGGL((gemm_prefill128_kernel<TNV, TMV, WNV, WMV, I32OUT>), dim3((unsigned)tiles),
                      dim3(pf128::THREADS), 0, s, xq, ldq, s_tok, wq, ldw, s_chan, M, N, K, y, ldy,
                      c, ldc, vec_out);
 }
 
-// 256-row tiles unless 192-row tiles (three quarters of the work each) fill
-// the chip in fewer rounds for this shape.
+// Tile of the full-line prefill kernel (measured on MI355X, Llama-3.1-8B
+// projections at M = 3000 and 4096):
+// * when 256 x 256 tiles take one round over the CUs and a three-quarter
+//   tile still does, the smaller tile: more CUs, less work each (M = 3000,
+//   N = 4096: 256 tiles of 256 x 192 tokens against 192 of 256 x 256,
+//   54 against 60 us for K = 4096, 163 against 175 us for K = 14336);
+// * otherwise 192 weight rows x 256 tokens when that needs fewer quarter-
+//   tile units of rounds (qkv: 103 against 118 us at M = 4096), else
+//   256 x 256. Per-tile time shrinks when fewer CUs share the memory
+//   system, so more rounds of smaller tiles rarely pay (gate_up at M = 3000:
+//   7 rounds of 256 x 192 took 377 us against 6 of 256 x 256 in 370).
 template <bool I32OUT>
 static void launch_prefill128_auto(const int8_t* xq, int64_t ldq, const float* s_tok,
                                    const int8_t* wq, int64_t ldw, const float* s_chan, int M,
                                    int N, int K, uint16_t* y, int64_t ldy, int32_t* c, int64_t ldc,
                                    bool vec_out, hipStream_t s) {
-  const int cus = device_cus();
-  const int tm = (M + pf128::TM - 1) / pf128::TM;
-  const int64_t rounds256 = ((int64_t)((N + 255) / 256) * tm + cus - 1) / cus;
-  const int64_t rounds192 = ((int64_t)((N + 191) / 192) * tm + cus - 1) / cus;
-  if (3 * rounds192 < 4 * rounds256)
-    launch_prefill128<192, I32OUT>(xq, ldq, s_tok, wq, ldw, s_chan, M, N, K, y, ldy, c, ldc,
-                                   vec_out, s);
+  const int64_t cus = device_cus();
+  auto tiles = [&](int tn, int tm) { return (int64_t)((N + tn - 1) / tn) * ((M + tm - 1) / tm); };
+  const int64_t t256 = tiles(256, 256), tm192 = tiles(256, 192), tn192 = tiles(192, 256);
+  bool use_m192 = false, use_n192 = false;
+  if (t256 <= cus) {
+    use_m192 = tm192 <= cus && tm192 > t256;
+    use_n192 = !use_m192 && tn192 <= cus && tn192 > t256;
+  } else {
+    use_n192 = 3 * ((tn192 + cus - 1) / cus) < 4 * ((t256 + cus - 1) / cus);
+  }
+  if (use_m192)
+    launch_prefill128<256, 192, 4, 2, I32OUT>(xq, ldq, s_tok, wq, ldw, s_chan, M, N, K, y, ldy, c,
+                                              ldc, vec_out, s);
+  else if (use_n192)
+    launch_prefill128<192, 256, 2, 4, I32OUT>(xq, ldq, s_tok, wq, ldw, s_chan, M, N, K, y, ldy, c,
+                                              ldc, vec_out, s);
   else
-    launch_prefill128<256, I32OUT>(xq, ldq, s_tok, wq, ldw, s_chan, M, N, K, y, ldy, c, ldc,
-                                   vec_out, s);
+    launch_prefill128<256, 256, 2, 4, I32OUT>(xq, ldq, s_tok, wq, ldw, s_chan, M, N, K, y, ldy, c,
+                                              ldc, vec_out, s);
 }
 
 template <int WN, int WM, bool I32OUT>

@@ -217,6 +217,40 @@ def test_gemm_bf16_epilogue(M, N, K):
     check_bf16(host(y), y64, y_ref)
 
 
+# The full-line prefill kernel picks one of three tiles (256 x 256, 192
+# weight rows x 256 tokens, 256 weight rows x 192 tokens) by rounds x tile
+# area over the CUs. On a 256-CU device each tile is the one chosen for one
+# of these shapes (ragged M and N included); at these sizes the oracle
+# recomputes every column of sampled token rows: both edges of the first
+# 192- and 256-row tiles and the last, partial tile.
+PF_TILE_SHAPES = [
+    (4000, 4000, 128),     # 256 x 256
+    (4096, 6144, 128),     # 192 x 256 (qkv at M = 4096)
+    (3000, 4096, 256),     # 256 x 192 (o and down at M = 3000)
+    (2990, 4090, 128),     # 256 x 192, ragged
+]
+
+
+@pytest.mark.parametrize("M,N,K", PF_TILE_SHAPES, ids=[f"M{m}_N{n}_K{k}" for m, n, k in PF_TILE_SHAPES])
+def test_gemm_prefill_tiles_sampled_rows(M, N, K):
+    a, b = i8((M, K), "pft_a"), i8((N, K), "pft_b")
+    r = WL.rng("pft_scales", M, N, K)
+    s_tok = np.exp(r.uniform(-12, -2, M)).astype(F32)
+    s_chan = np.exp(r.uniform(-10, -3, N)).astype(F32)
+    print(f"\n[prefill tiles] M={M} N={N} K={K}", flush=True)
+    acc = W.w8a8_gemm_i32(dev(a), dev(b))
+    y = W.w8a8_gemm(dev(a), dev(s_tok), dev(b), dev(s_chan))
+    torch().cuda.synchronize()
+    edges = [0, 1, 191, 192, 255, 256, 383, 384, M - 2, M - 1]
+    rows = np.unique(np.concatenate([edges, (M // 192) * 192 + np.arange(2), (M // 256) * 256 + np.arange(2),
+                                     r.choice(M, size=12, replace=False)]))
+    rows = rows[rows < M]
+    acc_ref = O.gemm_i32(a[rows], b)
+    np.testing.assert_array_equal(host(acc)[rows], acc_ref)
+    y64, y_ref = O.dequant_epilogue(acc_ref, s_tok[rows], s_chan)
+    check_bf16(host(y)[rows], y64, y_ref)
+
+
 def test_gemm_strided_output():
     M, N, K, ldy = 40, 200, 256, 264
     a, b = i8((M, K), "sa"), i8((N, K), "sb")
