@@ -205,15 +205,18 @@ __device__ __forceinline__ float exp_bounded(float x) {
 }
 
 // bf16(g / (1 + e^-g) * u) from a binary32 evaluation, when that is certain.
-// For |g| <= 80 the binary32 value is within 7 ulps of the real one (exp
-// 3 * 2^-24, then 1 + e, the division and the product one rounding each), so
-// its bf16 rounding is the real value's whenever its low 16 bits are more
-// than 16 away from 0x8000, the rounding boundary, and it is a normal number
-// of moderate size; a zero gate or up value gives an exact zero. ok = false
-// for everything else. tests/exhaustive/silu_fastpath_check.c runs this
-// decision for every pair of finite bf16 inputs.
+// The quotient is g times the hardware reciprocal of 1 + e, which the ISA
+// documents as within 1 ulp (so one of the two binary32 neighbours of the
+// exact reciprocal). For |g| <= 80 the binary32 value is then within 9 ulps
+// of the real one (relative errors: exp 3 * 2^-24, 1 + e 2^-24, the
+// reciprocal 2 * 2^-24, the two products 2^-24 each), so its bf16 rounding
+// is the real value's whenever its low 16 bits are more than 16 away from
+// 0x8000, the rounding boundary, and it is a normal number of moderate size;
+// a zero gate or up value gives an exact zero. ok = false for everything
+// else. tests/exhaustive/silu_fastpath_check.c runs this decision for every
+// pair of finite bf16 inputs and every reciprocal the 1-ulp bound allows.
 __device__ __forceinline__ float silu_mul_fast(float g, float u, bool& ok) {
-  const float q = g / (1.0f + exp_bounded(-g));
+  const float q = g * __builtin_amdgcn_rcpf(1.0f + exp_bounded(-g));
   const float m = q * u;
   const float a = fabsf(m);
   const int lo = (int)(__float_as_uint(m) & 0xFFFFu);

@@ -10,20 +10,24 @@
  *     e = exp_bounded(-g)      Cody-Waite reduction with a two-part ln 2,
  *                              degree-7 Taylor polynomial (Horner, fma),
  *                              scaling by 2^n
- *     q = RN(g / RN(1 + e)),  m32 = RN(q * u)
- * For |g| <= 80 the relative error of m32 is below 7 * 2^-24, so m32 lies
- * within 7 binary32 ulps of the real value. The kernel accepts
+ *     d = RN(1 + e),  c = rcp(d),  q = RN(g * c),  m32 = RN(q * u)
+ * where rcp is the hardware reciprocal, documented as within 1 ulp of 1/d:
+ * this program tries every binary32 value within 1 ulp of the exact 1/d
+ * (the two neighbours, or the exact value and its two neighbours). For
+ * |g| <= 80 the relative error of m32 is below 9 * 2^-24, so m32 lies
+ * within 9 binary32 ulps of the real value. The kernel accepts
  * bf16_rne(m32) when the low 16 bits of m32 are more than 16 away from
  * 0x8000 (the bf16 rounding boundary), |m32| is in [2^-120, 2^120) and
  * |g| <= 80, or when g or u is zero (an exact zero). Everything else is
  * evaluated in binary64.
  *
  * This program runs that decision for every pair of finite bf16 values
- * (g, u), 2^32 minus the non-finite ones, and compares every accepted
- * result with the binary64 evaluation (C's exp) rounded exactly to bf16.
- * It prints the number of mismatches (expected 0) and the share of pairs
- * the fast path takes. Build with -ffp-contract=off so that each binary32
- * step is the one the device performs.
+ * (g, u), 2^32 minus the non-finite ones, and every admissible reciprocal,
+ * and compares every accepted result with the binary64 evaluation (C's exp)
+ * rounded exactly to bf16. It prints the number of mismatches (expected 0)
+ * and the share of pairs the fast path takes (with the reciprocal rounded
+ * to nearest). Build with -ffp-contract=off so that each binary32 step is
+ * the one the device performs.
  */
 #include <math.h>
 #include <stdint.h>
@@ -70,7 +74,8 @@ static uint32_t bf16_rne_f64_normal(double v) {
   return (uint32_t)(sign << 15) | (fb >> 16);
 }
 
-static float qf[65536];      /* binary32 q = g / (1 + e^-g) per gate pattern, or NaN */
+#define NC 3
+static float qf[NC][65536];  /* q = g * c for each admissible reciprocal c of 1 + e^-g, or NaN */
 static double s64[65536];    /* binary64 g / (1 + exp(-g)) per gate pattern */
 static float uf[65536];
 static double ud[65536];
@@ -84,11 +89,22 @@ int main(void) {
     ud[p] = (double)v;
     const double g = (double)v;
     s64[p] = g / (1.0 + exp(-g));
+    for (int c = 0; c < NC; ++c) qf[c][p] = NAN;
     if (fabsf(v) <= 80.0f) {
-      const float e = exp_bounded(-v);
-      qf[p] = v / (1.0f + e);
-    } else {
-      qf[p] = NAN;
+      const float d = 1.0f + exp_bounded(-v);
+      const double r = 1.0 / (double)d;         /* exact to 2^-53, never a binary32 midpoint */
+      const float f = (float)r;
+      float cand[NC];
+      int n = 0;
+      if ((double)f == r) {                     /* exact: it and both neighbours */
+        cand[n++] = f;
+        cand[n++] = nextafterf(f, 0.0f);
+        cand[n++] = nextafterf(f, 2.0f);
+      } else {                                  /* the two neighbours of r */
+        cand[n++] = f;
+        cand[n++] = (double)f < r ? nextafterf(f, 2.0f) : nextafterf(f, 0.0f);
+      }
+      for (int c = 0; c < n; ++c) qf[c][p] = v * cand[c];
     }
   }
   long long mismatches = 0, accepted = 0, total = 0, in_range = 0, in_range_ok = 0;
@@ -96,41 +112,45 @@ int main(void) {
     reduction(+ : mismatches, accepted, total, in_range, in_range_ok)
   for (int gp = 0; gp < 65536; ++gp) {
     if (!finite_pat[gp]) continue;
-    const float q = qf[gp];
     const float g = uf[gp];
     for (int up = 0; up < 65536; ++up) {
       if (!finite_pat[up]) continue;
       ++total;
       const float u = uf[up];
-      if (isnan(q)) continue;                       /* |g| > 80: binary64 */
-      const float m = q * u;
-      int ok;
-      if (g == 0.0f || u == 0.0f) {
-        ok = 1;
-      } else {
-        const float a = fabsf(m);
-        const int lo = (int)(to_bits(m) & 0xFFFFu);
-        const int dist = lo > 0x8000 ? lo - 0x8000 : 0x8000 - lo;
-        const int range = a >= 0x1p-120f && a < 0x1p120f;
-        ok = range && dist > 16;
-        in_range += range;
-        in_range_ok += ok;
-      }
-      if (!ok) continue;
-      ++accepted;
-      const uint32_t fast = bf16_rne_f32(m);
-      const double m64 = s64[gp] * ud[up];
-      uint32_t want;
-      if (m64 == 0.0) {
-        want = signbit(m64) ? 0x8000u : 0u;
-      } else {
-        want = bf16_rne_f64_normal(m64);
-      }
-      if (fast != want) {
-        if (mismatches < 10)
-          printf("mismatch: g=%a u=%a fast=%04x want=%04x m32=%a m64=%a\n", (double)g, (double)u,
-                 fast, want, (double)m, m64);
-        ++mismatches;
+      for (int c = 0; c < NC; ++c) {
+        const float q = qf[c][gp];
+        if (isnan(q)) continue;                   /* |g| > 80 or no such candidate */
+        const float m = q * u;
+        int ok;
+        if (g == 0.0f || u == 0.0f) {
+          ok = 1;
+        } else {
+          const float a = fabsf(m);
+          const int lo = (int)(to_bits(m) & 0xFFFFu);
+          const int dist = lo > 0x8000 ? lo - 0x8000 : 0x8000 - lo;
+          const int range = a >= 0x1p-120f && a < 0x1p120f;
+          ok = range && dist > 16;
+          if (c == 0) {                           /* shares for the nearest reciprocal */
+            in_range += range;
+            in_range_ok += ok;
+          }
+        }
+        if (!ok) continue;
+        if (c == 0) ++accepted;
+        const uint32_t fast = bf16_rne_f32(m);
+        const double m64 = s64[gp] * ud[up];
+        uint32_t want;
+        if (m64 == 0.0) {
+          want = signbit(m64) ? 0x8000u : 0u;
+        } else {
+          want = bf16_rne_f64_normal(m64);
+        }
+        if (fast != want) {
+          if (mismatches < 10)
+            printf("mismatch: g=%a u=%a c=%d fast=%04x want=%04x m32=%a m64=%a\n", (double)g,
+                   (double)u, c, fast, want, (double)m, m64);
+          ++mismatches;
+        }
       }
     }
   }
