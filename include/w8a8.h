@@ -91,9 +91,11 @@ w8a8_status_t w8a8_quantize_act(const uint16_t* x, int64_t ldx, const float* smo
  * on int8 matrix units) and "Why activation quantization is hard" (the
  * per-token scale factors out of the channel sum and is applied after it);
  * part 2, "Inter-token latency (ITL)" (convert back to bf16).
- * Decode sizes (and K % 128 == 0 up to a few hundred tokens) take the
- * LDS-staged skinny kernels, larger M the tiled MFMA kernels; all give
- * identical results.
+ * With K % 128 == 0, decode sizes and batches up to about a thousand
+ * tokens take the LDS-staged kernel (token tiles of up to 64 rows), larger
+ * M the MFMA prefill kernel, whose tile shape the launcher picks from M, N
+ * and the CU count; other K take register- or LDS-staged kernels by M. All
+ * give identical results.
  *   xq [M, K] int8, ldq >= K;  s_tok [M] fp32          (read)
  *   wq [N, K] int8, ldw >= K;  s_chan [N] fp32         (read)
  *   y  [M, N] bf16, ldy >= N                           (written)
