@@ -43,7 +43,7 @@ Precision and rounding (the readings taken where the pages leave it open):
     whatever order the library uses.
   * Step 5 is a binary32 chain, float(acc) * S then * sw, each product
     rounded, then bf16 round-to-nearest-even (the "fp32, then rounded" value
-    outputs are judged against); a binary64 value is kept for error reports.
+    outputs are compared with); a binary64 value is kept for error reports.
   * bf16 values are handled as their uint16 bit patterns.
 
 Parity pins: every function here is checked in tests/test_oracle_pins.py
