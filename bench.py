@@ -61,9 +61,9 @@ def log(*a):
 # GEMM sources and the headers they include, comments and blank lines
 # removed) only; for any other code the field is null.
 MEASURED_TRAFFIC = {
-    "gemm_code_sha256": "21d1fdac4ecbbc20612fe9c6f76d7d243af132ab3613d196fa5e6a3721218a40",
-    "decode": 56294646,
-    "prefill": 427099900,
+    "gemm_code_sha256": "671a0d19013d2ccb4541afa5403895a4960de80ea8f1d187a4f52fc48fd22f26",
+    "decode": 56271898,
+    "prefill": 427654372,
 }
 GEMM_SRCS = [os.path.join("int8_w8a8_quantized_token_amd", "csrc", f)
              for f in ("gemm.hip", "gemm_common.h", "device_common.h")]

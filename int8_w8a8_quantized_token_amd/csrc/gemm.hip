@@ -1040,12 +1040,16 @@ static hipError_t launch_gemm_t(const int8_t* xq, int64_t ldq, const float* s_to
     // Shape classes measured on MI355X (Llama-3.1-8B projection shapes):
     // wide N takes 64 channels per workgroup once there are enough tokens to
     // reuse each weight fragment, mid N 32; otherwise 16 channels, so that
-    // N = 4096 still gives one workgroup per CU.
+    // N = 4096 still gives one workgroup per CU. Up to 16 tokens, 32 channels
+    // per workgroup for mid and wide N (gate_up at M = 16: 23.4 against
+    // 24.5 us with 16, whose token rows are then as many L2 lines as the
+    // weight rows), a fourth stage for deep K, and 4 waves everywhere
+    // (o: 5.7 against 5.8 us with 8 waves and 4 stages).
     const bool wide = N >= 16384, mid = N > 4096 && !wide, deep = K > 8192;
     if (M <= 16) {
-      if (mid) W8A8_MID(1, 2, 8, 3);
-      else if (wide || deep) W8A8_MID(1, 1, 4, 3);
-      else W8A8_MID(1, 1, 8, 4);
+      if (mid || wide) W8A8_MID(1, 2, 4, 3);
+      else if (deep) W8A8_MID(1, 1, 4, 4);
+      else W8A8_MID(1, 1, 4, 3);
     } else if (M <= 32) {
       if (wide) W8A8_MID(2, 4, 4, 3);
       else if (mid) W8A8_MID(2, 2, 4, 4);

@@ -160,6 +160,7 @@ GEMM_SHAPES = [
     (1, 16400, 128), (3, 5000, 8320), (7, 4100, 256), (16, 300, 384), (17, 16400, 1024),
     (24, 4500, 128), (31, 1000, 8320), (33, 16390, 512), (40, 6000, 256), (47, 200, 128),
     (49, 17000, 384), (55, 4200, 1152), (63, 100, 8320), (64, 16, 128),
+    (9, 2000, 8320), (2, 4096, 14336),
     # the same kernel in M tiles of 64 rows (ragged last tile), up to the
     # limits of its range, and the prefill kernel just past them (at
     # M < 512 for wide N)
