@@ -61,9 +61,9 @@ def log(*a):
 # GEMM sources and the headers they include, comments and blank lines
 # removed) only; for any other code the field is null.
 MEASURED_TRAFFIC = {
-    "gemm_code_sha256": "671a0d19013d2ccb4541afa5403895a4960de80ea8f1d187a4f52fc48fd22f26",
-    "decode": 56271898,
-    "prefill": 427654372,
+    "gemm_code_sha256": "d18726c503e0b9c54539f4b605dbab4bf85c6c546ef6607fc45b4f4f0f39a564",
+    "decode": 56275937,
+    "prefill": 427004847,
 }
 GEMM_SRCS = [os.path.join("int8_w8a8_quantized_token_amd", "csrc", f)
              for f in ("gemm.hip", "gemm_common.h", "device_common.h")]

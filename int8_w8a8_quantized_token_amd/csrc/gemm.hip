@@ -1067,10 +1067,18 @@ static hipError_t launch_gemm_t(const int8_t* xq, int64_t ldq, const float* s_to
       if (wide) W8A8_MID(4, 4, 2, 2);
       else if (mid) W8A8_MID(4, 4, 4, 2);
       else W8A8_MID(4, 2, 4, 3);
-    } else if (M <= 256 || (mid && M <= 512)) {
-      W8A8_MID(4, 4, 4, 2);
     } else {
-      W8A8_MID(4, 4, 2, 2);
+      // 64 channels x 64 tokens per workgroup with 4 waves (128 KB of LDS,
+      // one workgroup per CU) or 2 waves (two per CU, each pair taking about
+      // 1.5x the time of one 4-wave workgroup, measured on the Llama-3.1-8B
+      // projections): the one with fewer rounds over the CUs in those units
+      // (qkv at M = 256, 384 workgroups: 2 waves, 15.7 against 20.7 us; at
+      // M = 512, 768 workgroups: 4 waves, 30.0 against 31.1 us).
+      const int64_t groups = (int64_t)((N + 63) / 64) * ((M + 63) / 64), cus = device_cus();
+      if (2 * ((groups + cus - 1) / cus) <= 3 * ((groups + 2 * cus - 1) / (2 * cus)))
+        W8A8_MID(4, 4, 4, 2);
+      else
+        W8A8_MID(4, 4, 2, 2);
     }
 #undef W8A8_MID
   } else if (M <= kSkinnyMaxM) {
