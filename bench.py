@@ -21,6 +21,7 @@ duration is the graph time over the number of launches.
 """
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -93,6 +94,10 @@ def measured_traffic(root, which):
 
 def lin_bytes(M, N, K):
     return 2 * M * K + 4 * K + N * K + 4 * N + 2 * M * N
+
+
+def quant_bytes(M, K):
+    return 2 * M * K + 4 * K + M * K + 4 * M
 
 
 def gemm_bytes(M, N, K):
@@ -183,18 +188,56 @@ def capture(torch, fn):
     return g
 
 
-def time_graph(torch, g, steps, warmup):
+def time_graph(torch, g, steps, warmup, stats=False):
+    """Mean ms per replay over `steps` timed replays; with stats, also the
+    median, 95th percentile and mean of the single replays (one event after
+    each replay, inside the same timed region)."""
     for _ in range(warmup):
         g.replay()
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1 if stats else 2)]
+    ev[0].record()
+    for i in range(steps):
         g.replay()
-    e1.record()
+        if stats:
+            ev[i + 1].record()
+    ev[-1].record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps          # ms per replay
+    mean = ev[0].elapsed_time(ev[-1]) / steps
+    if not stats:
+        return mean
+    each = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    median = each[steps // 2] if steps % 2 else 0.5 * (each[steps // 2 - 1] + each[steps // 2])
+    p95 = each[math.ceil(0.95 * steps) - 1]             # nearest rank
+    return mean, {"median_ms": round(median, 4), "p95_ms": round(p95, 4),
+                  "mean_ms": round(mean, 4)}
+
+
+def dispatch_floor_us(torch, launches=512, steps=10):
+    """Per-launch time of a graph of one-element fills: the cost of a kernel
+    boundary in a graph, against which the small decode kernels are read."""
+    t = torch.zeros(1, dtype=torch.float32, device="cuda")
+    g = capture(torch, lambda: [t.fill_(0.0) for _ in range(launches)])
+    ms = time_graph(torch, g, steps, 2)
+    return round(ms / launches * 1e3, 3)
+
+
+def gpu_clocks():
+    """Current clocks (MHz) as amd-smi reports them: the shader clock of each
+    XCD and the memory clock; the error text instead when the tool is missing
+    or prints something else."""
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-g", "0", "-c", "--json"],
+                           capture_output=True, text=True, timeout=30)
+        doc, _ = json.JSONDecoder().raw_decode(r.stdout[r.stdout.index("{"):])
+        clocks = doc["gpu_data"][0]["clock"]
+        gfx = [clocks[k]["clk"]["value"] for k in sorted(clocks, key=lambda k: int(k.split("_")[-1]))
+               if k.startswith("gfx_") and isinstance(clocks[k].get("clk"), dict)]
+        mem = clocks.get("mem_0", {}).get("clk", {})
+        return {"gfx_per_xcd": gfx, "mem": mem.get("value") if isinstance(mem, dict) else None}
+    except Exception as e:                       # noqa: BLE001 -- reported, not raised
+        return {"error": f"{type(e).__name__}: {str(e)[:120]}"}
 
 
 def run_phase(torch, S, ms, steps, warmup, detail):
@@ -215,7 +258,7 @@ def run_phase(torch, S, ms, steps, warmup, detail):
         for proj, _, _ in S.shapes:
             S.quantize(proj, M)
     g_step = capture(torch, step)
-    ms_step = time_graph(torch, g_step, steps, warmup)
+    ms_step, step_stats = time_graph(torch, g_step, steps, warmup, stats=True)
     g_gemm = capture(torch, gemms)
     ms_gemm = time_graph(torch, g_gemm, steps, warmup)
     launches = len(ms) * LAYERS * len(S.shapes)
@@ -227,13 +270,17 @@ def run_phase(torch, S, ms, steps, warmup, detail):
                 t = time_graph(torch, g, max(steps // 4, 2), 2) / LAYERS
                 g2 = capture(torch, lambda: [S.gemm(proj, M, l) for l in range(LAYERS)])
                 t2 = time_graph(torch, g2, max(steps // 4, 2), 2) / LAYERS
+                g3 = capture(torch, lambda: [S.quantize(proj, M) for _ in range(LAYERS)])
+                t3 = time_graph(torch, g3, max(steps // 4, 2), 2) / LAYERS
                 per[f"{proj}_M{M}"] = {"linear_us": round(t * 1e3, 2), "gemm_us": round(t2 * 1e3, 2),
+                                       "quantize_us": round(t3 * 1e3, 2),
                                        "linear_GBps": round(lin_bytes(M, N, K) / (t * 1e-3) / 1e9, 1),
                                        "gemm_GBps": round(gemm_bytes(M, N, K) / (t2 * 1e-3) / 1e9, 1),
+                                       "quantize_GBps": round(quant_bytes(M, K) / (t3 * 1e-3) / 1e9, 1),
                                        "gemm_TOPS": round(2 * M * N * K / (t2 * 1e-3) / 1e12, 1)}
                 log(f"[bench] {proj:8s} M={M:5d}: linear {t*1e3:8.2f} us  gemm {t2*1e3:8.2f} us  "
                     f"{per[f'{proj}_M{M}']}")
-    return ms_step, ms_gemm, launches, per
+    return ms_step, ms_gemm, launches, per, step_stats
 
 
 def counters(torch, S, ms, layers=4):
@@ -366,8 +413,15 @@ def cpu_baseline(W, WL, sample_ms, min_seconds=10.0):
                 t += time.perf_counter() - t0
                 nbytes += lin_bytes(M, N, K)
         passes += 1
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")),
+                         model)
+    except OSError:
+        pass
     return {"value": round(nbytes / t / 1e9, 3), "unit": "GB/s", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": model, "cpus_in_affinity": len(os.sched_getaffinity(0)),
             "sample": f"{passes} pass(es) over one layer (qkv, o, gate_up, down) of the decode "
                       f"workload at M in {list(sample_ms)}: {passes * len(sample_ms) * 4} oracle "
                       f"linears, {nbytes / 1e9:.2f} GB algorithmic, {t:.1f} s of oracle time; "
@@ -396,7 +450,8 @@ def main():
         return
 
     # decode (headline)
-    d_step, d_gemm, d_launch, d_per = run_phase(torch, S, DECODE_MS, args.steps, args.warmup,
+    clocks_before = gpu_clocks()
+    d_step, d_gemm, d_launch, d_per, d_stats = run_phase(torch, S, DECODE_MS, args.steps, args.warmup,
                                                 args.detail)
     d_bytes = sum(lin_bytes(M, N, K) for M in DECODE_MS for _, N, K in S.shapes) * LAYERS
     d_gbytes = sum(gemm_bytes(M, N, K) for M in DECODE_MS for _, N, K in S.shapes) * LAYERS
@@ -421,6 +476,8 @@ def main():
                                                            len(S.shapes)),
                      "kernel": "gemm_mid_kernel", "launches_per_step": d_launch,
                      "avg_launch_us": round(d_gemm / d_launch * 1e3, 3)},
+        "step_stats": d_stats,
+        "dispatch_floor_us": dispatch_floor_us(torch),
     }
     if d_per:
         out["per_shape_decode"] = d_per
@@ -445,7 +502,7 @@ def main():
         out["chain"] = run_chain(torch, W, WL, S, args)
 
     if not args.no_prefill:
-        p_step, p_gemm, p_launch, p_per = run_phase(torch, S, (PREFILL_M,), max(args.steps // 4, 3),
+        p_step, p_gemm, p_launch, p_per, p_stats = run_phase(torch, S, (PREFILL_M,), max(args.steps // 4, 3),
                                                     min(args.warmup, 2), args.detail)
         ops = sum(2 * PREFILL_M * N * K for _, N, K in S.shapes) * LAYERS
         tops = ops / (p_step * 1e-3) / 1e12
@@ -454,6 +511,7 @@ def main():
             f"{p_gemm:.3f} ms -> {gtops:.0f} TOPS")
         out["prefill"] = {
             "value": round(tops, 1), "unit": "TOPS", "ms_per_step": round(p_step, 4),
+            "step_stats": p_stats,
             "config": {"workload": "llama8b_prefill: same 32 layers x 4 projections at M=4096",
                        "m": PREFILL_M},
             "roofline": {"bound": "mfma", "achieved": round(gtops, 1), "peak": INT8_PEAK_TOPS,
@@ -467,6 +525,8 @@ def main():
         }
         if p_per:
             out["per_shape_prefill"] = p_per
+
+    out["clocks_mhz"] = {"before": clocks_before, "after": gpu_clocks()}
 
     if not args.no_cpu_baseline:
         t0 = time.time()
