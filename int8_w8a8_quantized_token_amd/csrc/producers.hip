@@ -132,16 +132,31 @@ __global__ __launch_bounds__(BS) void rmsnorm_quantize_kernel(
   const int nvec = K / 8;
   uint16_t* hr = h + row * ldh;
 
+  // Every load a thread needs (its h, residual and factor vectors) goes out
+  // before any arithmetic: one memory round trip per row, not one per vector
+  // plus one for the factors after the reduction. Vectors past the row end
+  // load the row's last vector (K >= 16) and are then left out.
+  uint4 hraw[NV], rraw[NV];
+  float gv[NV][8];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int vl = min(tid + i * BS, nvec - 1);
+    hraw[i] = *reinterpret_cast<const uint4*>(hr + (int64_t)vl * 8);
+    if constexpr (ADD) rraw[i] = *reinterpret_cast<const uint4*>(res + row * ldr + (int64_t)vl * 8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) gv[i][e] = g[vl * 8 + e];
+  }
+
   float v[NV][8];
   DD acc = {0.0, 0.0};
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int vi = tid + i * BS;
     if (vi < nvec) {
-      unpack8(*reinterpret_cast<const uint4*>(hr + (int64_t)vi * 8), v[i]);
+      unpack8(hraw[i], v[i]);
       if constexpr (ADD) {
         float r[8];
-        unpack8(*reinterpret_cast<const uint4*>(res + row * ldr + (int64_t)vi * 8), r);
+        unpack8(rraw[i], r);
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[i][e] = __uint_as_float(f32_to_bf16_rne(v[i][e] + r[e]) << 16);
         *reinterpret_cast<uint4*>(hr + (int64_t)vi * 8) = pack8_bf16(v[i]);
@@ -164,7 +179,7 @@ __global__ __launch_bounds__(BS) void rmsnorm_quantize_kernel(
     if (vi < nvec) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        v[i][e] = (v[i][e] * inv) * g[vi * 8 + e];
+        v[i][e] = (v[i][e] * inv) * gv[i][e];
         amax = fmaxf(amax, fabsf(v[i][e]));
       }
     }
