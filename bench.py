@@ -43,6 +43,7 @@ def parse():
                    help="skip timing the CPU oracle")
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-chain", action="store_true", help="skip the 32-layer block chain")
+    p.add_argument("--no-70b", action="store_true", help="skip the Llama-3-70B projections")
     p.add_argument("--detail", action="store_true", help="per-shape timings on stderr")
     p.add_argument("--counters", action="store_true",
                    help="eager launches for hardware-counter runs (rocprofv3 --pmc); no timing")
@@ -379,6 +380,68 @@ def run_chain(torch, W, WL, S, args):
                        "tokens": M}}
 
 
+def run_70b(torch, W, WL, args):
+    """Llama-3-70B per-layer projections (qkv 8192->10240, o 8192->8192,
+    gate_up 8192->57344, down 28672->8192): w8a8_linear at 32 tokens (GB/s of
+    algorithmic bytes) and at 2048 tokens (int8 TOPS). Each shape rotates over
+    max(2, ceil(1 GiB / weight bytes)) distinct weight buffers so every call
+    streams its weights from HBM."""
+    import math as _m
+    wl = WL.WORKLOADS["llama70b"]
+    m_dec, m_pf = wl.ms
+    per_dec, per_pf = {}, {}
+    dec_bytes = dec_us = pf_ops = pf_us = 0.0
+    t0 = time.time()
+    for proj, N, K in wl.shapes:
+        outl = WL.outlier_channels(K, wl.outlier_frac, wl.name)
+        xcal = WL.activations(m_pf, K, wl.name, proj, 0, outliers=outl, mult=wl.outlier_mult)
+        w = WL.weights(N, K, wl.w_std, wl.name, proj, 0)
+        xcal_d = _bf16_dev(torch, xcal)
+        w_d = _bf16_dev(torch, w)
+        del w
+        s = W.w8a8_smoothing_factors(W.w8a8_channel_absmax(xcal_d), W.w8a8_channel_absmax(w_d))
+        wq, sw = W.w8a8_quantize_weight(w_d, s)
+        del w_d
+        copies = max(2, _m.ceil(2**30 / (N * K)))
+        wqs = [wq] + [wq.clone() for _ in range(copies - 1)]
+        for M in (m_dec, m_pf):
+            x = xcal_d[:M].clone() if M == m_pf else _bf16_dev(torch, WL.activations(
+                M, K, wl.name, proj, 0, outliers=outl, mult=wl.outlier_mult))
+            y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+            ws = torch.empty((W.w8a8_linear_workspace_bytes(M, K),), dtype=torch.uint8, device="cuda")
+            g = capture(torch, lambda: [W.w8a8_linear(x, s, wqs[c], sw, y=y, workspace=ws)
+                                        for c in range(copies)])
+            us = time_graph(torch, g, max(args.steps // 4, 3), 2) / copies * 1e3
+            del g
+            if M == m_dec:
+                b = lin_bytes(M, N, K)
+                per_dec[proj] = {"us": round(us, 2), "GBps": round(b / (us * 1e-6) / 1e9, 1)}
+                dec_bytes += b
+                dec_us += us
+            else:
+                ops = 2.0 * M * N * K
+                per_pf[proj] = {"us": round(us, 2), "TOPS": round(ops / (us * 1e-6) / 1e12, 1)}
+                pf_ops += ops
+                pf_us += us
+        del wqs, xcal_d
+        torch.cuda.empty_cache()
+    out = {"decode": {"M": m_dec, "value": round(dec_bytes / (dec_us * 1e-6) / 1e9, 1),
+                      "unit": "GB/s", "per_shape": per_dec},
+           "prefill": {"M": m_pf, "value": round(pf_ops / (pf_us * 1e-6) / 1e12, 1),
+                       "unit": "TOPS", "per_shape": per_pf},
+           "config": {"workload": "llama70b: Llama-3-70B qkv/o/gate_up/down, one layer, "
+                                  "w8a8_linear per projection, weights rotated over >= 1 GiB"}}
+    log(f"[bench] llama70b ({time.time() - t0:.1f}s): decode M={m_dec} "
+        f"{out['decode']['value']:.0f} GB/s {per_dec}; prefill M={m_pf} "
+        f"{out['prefill']['value']:.0f} TOPS {per_pf}")
+    return out
+
+
+def _bf16_dev(torch, u16):
+    import numpy as np
+    return torch.from_numpy(np.ascontiguousarray(u16).view(np.int16)).cuda().view(torch.bfloat16)
+
+
 def cpu_baseline(W, WL, sample_ms, min_seconds=10.0):
     """The oracle, timed on this host on one layer of the decode workload."""
     import numpy as np
@@ -500,6 +563,8 @@ def main():
 
     if not args.no_chain:
         out["chain"] = run_chain(torch, W, WL, S, args)
+    if not args.no_70b:
+        out["llama70b"] = run_70b(torch, W, WL, args)
 
     if not args.no_prefill:
         p_step, p_gemm, p_launch, p_per, p_stats = run_phase(torch, S, (PREFILL_M,), max(args.steps // 4, 3),

@@ -1037,35 +1037,50 @@ static hipError_t launch_gemm_t(const int8_t* xq, int64_t ldq, const float* s_to
 #define W8A8_MID(MTV, RWV, NWV, NSV)                                                          \
   launch_mid<MTV, RWV, NWV, NSV, I32OUT>(xq, ldq, s_tok, wq, ldw, s_chan, M, N, K, y, ldy, c, ldc, \
                                          vec_out, s)
-    // Shape classes measured on MI355X (Llama-3.1-8B projection shapes):
-    // wide N takes 64 channels per workgroup once there are enough tokens to
-    // reuse each weight fragment, mid N 32; otherwise 16 channels, so that
-    // N = 4096 still gives one workgroup per CU. Up to 16 tokens, 32 channels
-    // per workgroup for mid and wide N (gate_up at M = 16: 23.4 against
-    // 24.5 us with 16, whose token rows are then as many L2 lines as the
-    // weight rows), a fourth stage for deep K, and 4 waves everywhere
-    // (o: 5.7 against 5.8 us with 8 waves and 4 stages).
-    const bool wide = N >= 16384, mid = N > 4096 && !wide, deep = K > 8192;
-    if (M <= 16) {
-      if (mid || wide) W8A8_MID(1, 2, 4, 3);
+    // Up to 64 tokens one M tile of 16 * MT rows covers the tokens, and the
+    // channels per workgroup (16 * RW) come from a cost model. Each
+    // workgroup streams its 16 * RW weight rows and loads its 16 * MT token
+    // rows, so the busiest CU moves rounds(RW) * (16 * RW + 16 * MT) rows,
+    // rounds(RW) being the workgroups per CU rounded up; the smallest cost
+    // wins, ties going to fewer channels. For one token group only RW = 1
+    // or 2 compete (64 channels measured slower there: 4096 -> 28672 at one
+    // token 23.2 against 21.1 us). Measured on MI355X over the Llama-3.1-8B
+    // and Llama-3-70B projections at M in {1, 4, 16, 32, 64}, the model
+    // picks the fastest RW everywhere but 8192 -> 57344 at M <= 4 (6% behind
+    // 16 channels); it reproduces the earlier fixed N classes on the 8B
+    // shapes and takes 8192 -> 10240 at 32 tokens from 24.6 to 21.4 us and
+    // at 64 from 31.0 to 26.2. Waves and stages per (MT, RW) are the
+    // measured best: a fourth stage for K > 8192 at RW = 1, 8 waves for 32
+    // tokens at RW = 1 and short K, 2 waves at RW = 4 from 48 tokens.
+    const bool deep = K > 8192;
+    const int mt = (M + 15) / 16;
+    const int64_t cus = device_cus();
+    auto cost = [&](int rw) {
+      const int64_t groups = (N + 16 * rw - 1) / (16 * rw);
+      return (groups + cus - 1) / cus * (16 * rw + 16 * mt);
+    };
+    int rw = cost(2) < cost(1) ? 2 : 1;
+    if (mt > 1 && cost(4) < cost(rw)) rw = 4;
+    if (mt == 1) {
+      if (rw == 2) W8A8_MID(1, 2, 4, 3);
       else if (deep) W8A8_MID(1, 1, 4, 4);
       else W8A8_MID(1, 1, 4, 3);
-    } else if (M <= 32) {
-      if (wide) W8A8_MID(2, 4, 4, 3);
-      else if (mid) W8A8_MID(2, 2, 4, 4);
+    } else if (mt == 2) {
+      if (rw == 4) W8A8_MID(2, 4, 4, 3);
+      else if (rw == 2) W8A8_MID(2, 2, 4, 4);
       else if (deep) W8A8_MID(2, 1, 4, 4);
       else W8A8_MID(2, 1, 8, 3);
-    } else if (M <= 48) {
-      if (wide) W8A8_MID(3, 4, 2, 3);
-      else if (mid) W8A8_MID(3, 2, 4, 3);
+    } else if (mt == 3) {
+      if (rw == 4) W8A8_MID(3, 4, 2, 3);
+      else if (rw == 2) W8A8_MID(3, 2, 4, 3);
       else W8A8_MID(3, 1, 4, 3);
     } else if (M <= kSkinnyMaxM) {
-      if (wide) W8A8_MID(4, 4, 2, 2);
-      else if (mid) W8A8_MID(4, 2, 4, 3);
+      if (rw == 4) W8A8_MID(4, 4, 2, 2);
+      else if (rw == 2) W8A8_MID(4, 2, 4, 3);
       else W8A8_MID(4, 1, 4, 3);
     } else if (M <= 128) {     // several M tiles of 64 rows from here on
-      if (wide) W8A8_MID(4, 4, 2, 2);
-      else if (mid) W8A8_MID(4, 4, 4, 2);
+      if (N >= 16384) W8A8_MID(4, 4, 2, 2);
+      else if (N > 4096) W8A8_MID(4, 4, 4, 2);
       else W8A8_MID(4, 2, 4, 3);
     } else {
       // 64 channels x 64 tokens per workgroup with 4 waves (128 KB of LDS,
@@ -1074,7 +1089,7 @@ static hipError_t launch_gemm_t(const int8_t* xq, int64_t ldq, const float* s_to
       // projections): the one with fewer rounds over the CUs in those units
       // (qkv at M = 256, 384 workgroups: 2 waves, 15.7 against 20.7 us; at
       // M = 512, 768 workgroups: 4 waves, 30.0 against 31.1 us).
-      const int64_t groups = (int64_t)((N + 63) / 64) * ((M + 63) / 64), cus = device_cus();
+      const int64_t groups = (int64_t)((N + 63) / 64) * ((M + 63) / 64);
       if (2 * ((groups + cus - 1) / cus) <= 3 * ((groups + 2 * cus - 1) / (2 * cus)))
         W8A8_MID(4, 4, 4, 2);
       else
