@@ -74,20 +74,25 @@ def test_more_than_one_gpu_is_refused():
     assert "one GPU" in r.stderr
 
 
-def test_stored_traffic_follows_the_code(tmp_path):
-    # The stored figures are reported for the GEMM code they were taken with
-    # and for no other; comments and blank lines do not count as code.
-    assert bench.measured_traffic(ROOT, "decode") == bench.MEASURED_TRAFFIC["decode"]
+def test_stored_traffic_follows_the_code(tmp_path, monkeypatch):
+    # Stored counter figures are reported for the GEMM code they were taken
+    # with and for no other; comments and blank lines do not count as code.
     for rel in bench.GEMM_SRCS:
         dst = tmp_path / rel
         dst.parent.mkdir(parents=True, exist_ok=True)
         dst.write_text(open(os.path.join(ROOT, rel)).read())
-    assert bench.measured_traffic(str(tmp_path), "prefill") == bench.MEASURED_TRAFFIC["prefill"]
+    stored = dict(bench.MEASURED_TRAFFIC, decode=111, prefill=222,
+                  gemm_code_sha256=bench.code_sha256([str(tmp_path / r) for r in bench.GEMM_SRCS]))
+    monkeypatch.setattr(bench, "MEASURED_TRAFFIC", stored)
+    assert bench.measured_traffic(str(tmp_path), "decode") == 111
+    assert bench.measured_traffic(str(tmp_path), "prefill") == 222
     gemm = tmp_path / bench.GEMM_SRCS[0]
     gemm.write_text(gemm.read_text() + "\n// a comment\n\n")
-    assert bench.measured_traffic(str(tmp_path), "decode") == bench.MEASURED_TRAFFIC["decode"]
+    assert bench.measured_traffic(str(tmp_path), "decode") == 111
     gemm.write_text(gemm.read_text() + "static int unused_marker;\n")
     assert bench.measured_traffic(str(tmp_path), "decode") is None
+    monkeypatch.setattr(bench, "MEASURED_TRAFFIC", {})
+    assert bench.measured_traffic(ROOT, "decode") is None
 
 
 def test_clock_readout_never_raises():
