@@ -40,7 +40,10 @@ QA_SHAPES = [(1, 16), (2, 48), (3, 64), (15, 4096 + 16), (16, 4096), (17, 2048),
              # many rows: several rows per workgroup, ragged M and channel tails,
              # and K beyond the register-resident limit
              (513, 4096), (1024, 4096 + 16), (1100, 14336), (2049, 2048), (8200, 64),
-             (600, 40960)]
+             (600, 40960),
+             # few rows longer than 1024 threads hold in registers (read twice),
+             # up to the largest K the library accepts
+             (5, 65536 + 16), (1, 131072)]
 
 
 @pytest.mark.parametrize("M,K", QA_SHAPES, ids=[f"M{m}_K{k}" for m, k in QA_SHAPES])
@@ -205,6 +208,21 @@ def test_gemm_i32_closed_form_extremes():
         assert np.all(acc == want[None, :])
 
 
+@pytest.mark.parametrize("K", [131072, 131072 - 16], ids=["K131072", "K131056"])
+def test_gemm_i32_extremes_at_max_k(K):
+    # The largest K the library accepts keeps 127 * 127 * K inside int32;
+    # every token count class (decode, M-tiled or tiled, prefill) at that K.
+    for M in (1, 96, 1600):
+        a = np.full((M, K), 127, np.int8)
+        b = np.full((40, K), -127, np.int8)
+        b[::2] = 127
+        acc = host(W.w8a8_gemm_i32(dev(a), dev(b)))
+        torch().cuda.synchronize()
+        want = np.where(np.arange(40) % 2 == 0, 16129 * K, -16129 * K)
+        assert want.max() < 2**31
+        assert np.all(acc == want[None, :]), (M, K)
+
+
 @pytest.mark.parametrize("M,N,K", GEMM_SHAPES, ids=[f"M{m}_N{n}_K{k}" for m, n, k in GEMM_SHAPES])
 def test_gemm_bf16_epilogue(M, N, K):
     a, b = i8((M, K), "a"), i8((N, K), "b")
@@ -365,7 +383,8 @@ def test_smoothing_factor_edge_values():
 # ---------------------------------------------------------------------------
 
 LIN_SHAPES = [(1, 64, 4096), (16, 4096, 4096), (17, 300, 1040), (64, 1024, 14336),
-              (65, 512, 2048), (300, 700, 4096)]
+              (65, 512, 2048), (300, 700, 4096),
+              (2, 64, 131072)]          # the largest K the library accepts
 
 
 @pytest.mark.parametrize("M,N,K", LIN_SHAPES, ids=[f"M{m}_N{n}_K{k}" for m, n, k in LIN_SHAPES])
