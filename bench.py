@@ -63,9 +63,9 @@ def log(*a):
 # GEMM sources and the headers they include, comments and blank lines
 # removed) only; for any other code the field is null.
 MEASURED_TRAFFIC = {
-    "gemm_code_sha256": "2526db7e1cb4581ba28e76aafe374cfd35148a6913189f79708bf9e50ac94a71",
-    "decode": 56276812,
-    "prefill": 426694602,
+    "gemm_code_sha256": "028a49d7fa37fe5c779f147238e958ad0752ad8547ba7f9f85a00ab61c3afbad",
+    "decode": 56276934,
+    "prefill": 427494906,
 }
 GEMM_SRCS = [os.path.join("int8_w8a8_quantized_token_amd", "csrc", f)
              for f in ("gemm.hip", "gemm_common.h", "device_common.h")]

@@ -31,6 +31,8 @@
 //   16x16: i = 4*(l/16) + e
 //   32x32: i = 8*(e/4) + 4*(l/32) + (e%4).
 
+#include <atomic>
+
 #include "device_common.h"
 #include "gemm_common.h"
 #include "launchers.h"
@@ -921,13 +923,20 @@ __global__ __launch_bounds__(NW * kWave) void gemm_mid_kernel(
     }
 }
 
-// Compute units of the current device.
+// Compute units of the current device, queried once per device and kept
+// (the launchers call this on every GEMM; concurrent first calls store the
+// same value).
 static int device_cus() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cached[kMaxDevices];
   int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev >= 0 && dev < kMaxDevices && (cus = cached[dev].load(std::memory_order_relaxed)) > 0)
+    return cus;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       cus <= 0)
     cus = 256;
+  if (dev >= 0 && dev < kMaxDevices) cached[dev].store(cus, std::memory_order_relaxed);
   return cus;
 }
 
