@@ -63,12 +63,12 @@ def log(*a):
 # GEMM sources and the headers they include, comments and blank lines
 # removed) only; for any other code the field is null.
 MEASURED_TRAFFIC = {
-    "gemm_code_sha256": "028a49d7fa37fe5c779f147238e958ad0752ad8547ba7f9f85a00ab61c3afbad",
-    "decode": 56276934,
-    "prefill": 427494906,
+    "gemm_code_sha256": "9ff7b2e49c608bc1e309dcfb26cb84837d83a67c284e2a08b68ff26e9374bf10",
+    "decode": 56275613,
+    "prefill": 427171128,
 }
 GEMM_SRCS = [os.path.join("int8_w8a8_quantized_token_amd", "csrc", f)
-             for f in ("gemm.hip", "gemm_common.h", "device_common.h")]
+             for f in ("gemm.hip", "gemm_common.h", "gemm_dispatch.h", "device_common.h")]
 
 
 def code_sha256(paths):

@@ -35,6 +35,7 @@
 
 #include "device_common.h"
 #include "gemm_common.h"
+#include "gemm_dispatch.h"
 #include "launchers.h"
 
 namespace w8a8 {
@@ -950,41 +951,25 @@ static void launch_prefill128(const int8_t* xq, int64_t ldq, const float* s_tok,
                      c, ldc, vec_out);
 }
 
-// Tile of the full-line prefill kernel (measured on MI355X, Llama-3.1-8B
-// projections at M = 3000 and 4096):
-// * when 256 x 256 tiles take one round over the CUs and a three-quarter
-//   tile still does, the smaller tile: more CUs, less work each (M = 3000,
-//   N = 4096: 256 tiles of 256 x 192 tokens against 192 of 256 x 256,
-//   54 against 60 us for K = 4096, 163 against 175 us for K = 14336);
-// * otherwise 192 weight rows x 256 tokens when that needs fewer quarter-
-//   tile units of rounds (qkv: 103 against 118 us at M = 4096), else
-//   256 x 256. Per-tile time shrinks when fewer CUs share the memory
-//   system, so more rounds of smaller tiles rarely pay (gate_up at M = 3000:
-//   7 rounds of 256 x 192 took 377 us against 6 of 256 x 256 in 370).
+// Tile of the full-line prefill kernel: dispatch::prefill_tile.
 template <bool I32OUT>
 static void launch_prefill128_auto(const int8_t* xq, int64_t ldq, const float* s_tok,
                                    const int8_t* wq, int64_t ldw, const float* s_chan, int M,
                                    int N, int K, uint16_t* y, int64_t ldy, int32_t* c, int64_t ldc,
                                    bool vec_out, hipStream_t s) {
-  const int64_t cus = device_cus();
-  auto tiles = [&](int tn, int tm) { return (int64_t)((N + tn - 1) / tn) * ((M + tm - 1) / tm); };
-  const int64_t t256 = tiles(256, 256), tm192 = tiles(256, 192), tn192 = tiles(192, 256);
-  bool use_m192 = false, use_n192 = false;
-  if (t256 <= cus) {
-    use_m192 = tm192 <= cus && tm192 > t256;
-    use_n192 = !use_m192 && tn192 <= cus && tn192 > t256;
-  } else {
-    use_n192 = 3 * ((tn192 + cus - 1) / cus) < 4 * ((t256 + cus - 1) / cus);
+  switch (dispatch::prefill_tile(M, N, device_cus())) {
+    case dispatch::PrefillTile::k256x192:
+      launch_prefill128<256, 192, 4, 2, I32OUT>(xq, ldq, s_tok, wq, ldw, s_chan, M, N, K, y, ldy,
+                                                c, ldc, vec_out, s);
+      break;
+    case dispatch::PrefillTile::k192x256:
+      launch_prefill128<192, 256, 2, 4, I32OUT>(xq, ldq, s_tok, wq, ldw, s_chan, M, N, K, y, ldy,
+                                                c, ldc, vec_out, s);
+      break;
+    default:
+      launch_prefill128<256, 256, 2, 4, I32OUT>(xq, ldq, s_tok, wq, ldw, s_chan, M, N, K, y, ldy,
+                                                c, ldc, vec_out, s);
   }
-  if (use_m192)
-    launch_prefill128<256, 192, 4, 2, I32OUT>(xq, ldq, s_tok, wq, ldw, s_chan, M, N, K, y, ldy, c,
-                                              ldc, vec_out, s);
-  else if (use_n192)
-    launch_prefill128<192, 256, 2, 4, I32OUT>(xq, ldq, s_tok, wq, ldw, s_chan, M, N, K, y, ldy, c,
-                                              ldc, vec_out, s);
-  else
-    launch_prefill128<256, 256, 2, 4, I32OUT>(xq, ldq, s_tok, wq, ldw, s_chan, M, N, K, y, ldy, c,
-                                              ldc, vec_out, s);
 }
 
 template <int WN, int WM, bool I32OUT>
@@ -1001,7 +986,7 @@ static void launch_prefill(const int8_t* xq, int64_t ldq, const float* s_tok, co
 // Dispatch
 // ---------------------------------------------------------------------------
 
-constexpr int kSkinnyMaxM = 64;
+using dispatch::kSkinnyMaxM;
 constexpr int kPrefillMinM = 512;
 
 template <int MT, int RW, int NW, int U, bool I32OUT, bool LATE = false>
@@ -1025,16 +1010,16 @@ static void launch_mid(const int8_t* xq, int64_t ldq, const float* s_tok, const 
                      wq, ldw, s_chan, M, N, K, y, ldy, c, ldc, vec_out, rot);
 }
 
-// Which M take the mid kernel (K % 128 == 0): every decode M, and beyond
-// that while M tiles of 64 rows beat the prefill kernel's 256-row tiles,
-// which fill the 256 CUs only once there are enough of them (measured on
-// MI355X, Llama-3.1-8B shapes: up to M = 128 for 28672 channels, 1536 for
-// K = 14336, 1024 otherwise).
-static bool mid_path(int M, int N, int K) {
-  if (K % MidCfg<1, 1, 1, 2>::kBK != 0) return false;
-  if (M <= kSkinnyMaxM) return true;
-  if (N >= 16384) return M <= 128;
-  return M <= (K > 8192 ? 1536 : 1024);
+// One decode-kernel instance if its template arguments are the chosen ones.
+template <int MT, int RW, int NW, int NS, bool I32OUT>
+static bool launch_mid_if(const dispatch::MidConfig& m, const int8_t* xq, int64_t ldq,
+                          const float* s_tok, const int8_t* wq, int64_t ldw, const float* s_chan,
+                          int M, int N, int K, uint16_t* y, int64_t ldy, int32_t* c, int64_t ldc,
+                          bool vec_out, hipStream_t s) {
+  if (m.mt != MT || m.rw != RW || m.nw != NW || m.ns != NS) return false;
+  launch_mid<MT, RW, NW, NS, I32OUT>(xq, ldq, s_tok, wq, ldw, s_chan, M, N, K, y, ldy, c, ldc,
+                                     vec_out, s);
+  return true;
 }
 
 template <bool I32OUT>
@@ -1042,69 +1027,20 @@ static hipError_t launch_gemm_t(const int8_t* xq, int64_t ldq, const float* s_to
                                 const int8_t* wq, int64_t ldw, const float* s_chan, int M,
                                 int N, int K, uint16_t* y, int64_t ldy, int32_t* c, int64_t ldc,
                                 bool vec_out, hipStream_t s) {
-  if (mid_path(M, N, K)) {
-#define W8A8_MID(MTV, RWV, NWV, NSV)                                                          \
-  launch_mid<MTV, RWV, NWV, NSV, I32OUT>(xq, ldq, s_tok, wq, ldw, s_chan, M, N, K, y, ldy, c, ldc, \
-                                         vec_out, s)
-    // Up to 64 tokens one M tile of 16 * MT rows covers the tokens, and the
-    // channels per workgroup (16 * RW) come from a cost model. Each
-    // workgroup streams its 16 * RW weight rows and loads its 16 * MT token
-    // rows, so the busiest CU moves rounds(RW) * (16 * RW + 16 * MT) rows,
-    // rounds(RW) being the workgroups per CU rounded up; the smallest cost
-    // wins, ties going to fewer channels. For one token group only RW = 1
-    // or 2 compete (64 channels measured slower there: 4096 -> 28672 at one
-    // token 23.2 against 21.1 us). Measured on MI355X over the Llama-3.1-8B
-    // and Llama-3-70B projections at M in {1, 4, 16, 32, 64}, the model
-    // picks the fastest RW everywhere but 8192 -> 57344 at M <= 4 (6% behind
-    // 16 channels); it reproduces the earlier fixed N classes on the 8B
-    // shapes and takes 8192 -> 10240 at 32 tokens from 24.6 to 21.4 us and
-    // at 64 from 31.0 to 26.2. Waves and stages per (MT, RW) are the
-    // measured best: a fourth stage for K > 8192 at RW = 1, 8 waves for 32
-    // tokens at RW = 1 and short K, 2 waves at RW = 4 from 48 tokens.
-    const bool deep = K > 8192;
-    const int mt = (M + 15) / 16;
-    const int64_t cus = device_cus();
-    auto cost = [&](int rw) {
-      const int64_t groups = (N + 16 * rw - 1) / (16 * rw);
-      return (groups + cus - 1) / cus * (16 * rw + 16 * mt);
-    };
-    int rw = cost(2) < cost(1) ? 2 : 1;
-    if (mt > 1 && cost(4) < cost(rw)) rw = 4;
-    if (mt == 1) {
-      if (rw == 2) W8A8_MID(1, 2, 4, 3);
-      else if (deep) W8A8_MID(1, 1, 4, 4);
-      else W8A8_MID(1, 1, 4, 3);
-    } else if (mt == 2) {
-      if (rw == 4) W8A8_MID(2, 4, 4, 3);
-      else if (rw == 2) W8A8_MID(2, 2, 4, 4);
-      else if (deep) W8A8_MID(2, 1, 4, 4);
-      else W8A8_MID(2, 1, 8, 3);
-    } else if (mt == 3) {
-      if (rw == 4) W8A8_MID(3, 4, 2, 3);
-      else if (rw == 2) W8A8_MID(3, 2, 4, 3);
-      else W8A8_MID(3, 1, 4, 3);
-    } else if (M <= kSkinnyMaxM) {
-      if (rw == 4) W8A8_MID(4, 4, 2, 2);
-      else if (rw == 2) W8A8_MID(4, 2, 4, 3);
-      else W8A8_MID(4, 1, 4, 3);
-    } else if (M <= 128) {     // several M tiles of 64 rows from here on
-      if (N >= 16384) W8A8_MID(4, 4, 2, 2);
-      else if (N > 4096) W8A8_MID(4, 4, 4, 2);
-      else W8A8_MID(4, 2, 4, 3);
-    } else {
-      // 64 channels x 64 tokens per workgroup with 4 waves (128 KB of LDS,
-      // one workgroup per CU) or 2 waves (two per CU, each pair taking about
-      // 1.5x the time of one 4-wave workgroup, measured on the Llama-3.1-8B
-      // projections): the one with fewer rounds over the CUs in those units
-      // (qkv at M = 256, 384 workgroups: 2 waves, 15.7 against 20.7 us; at
-      // M = 512, 768 workgroups: 4 waves, 30.0 against 31.1 us).
-      const int64_t groups = (int64_t)((N + 63) / 64) * ((M + 63) / 64);
-      if (2 * ((groups + cus - 1) / cus) <= 3 * ((groups + 2 * cus - 1) / (2 * cus)))
-        W8A8_MID(4, 4, 4, 2);
-      else
-        W8A8_MID(4, 4, 2, 2);
-    }
+  if (dispatch::mid_path(M, N, K)) {
+    // Every configuration dispatch::mid_config can return has an instance.
+    const dispatch::MidConfig m = dispatch::mid_config(M, N, K, device_cus());
+#define W8A8_MID(MTV, RWV, NWV, NSV)                                                       \
+  launch_mid_if<MTV, RWV, NWV, NSV, I32OUT>(m, xq, ldq, s_tok, wq, ldw, s_chan, M, N, K, y, \
+                                            ldy, c, ldc, vec_out, s)
+    const bool launched =
+        W8A8_MID(1, 2, 4, 3) || W8A8_MID(1, 1, 4, 4) || W8A8_MID(1, 1, 4, 3) ||
+        W8A8_MID(2, 4, 4, 3) || W8A8_MID(2, 2, 4, 4) || W8A8_MID(2, 1, 4, 4) ||
+        W8A8_MID(2, 1, 8, 3) || W8A8_MID(3, 4, 2, 3) || W8A8_MID(3, 2, 4, 3) ||
+        W8A8_MID(3, 1, 4, 3) || W8A8_MID(4, 4, 2, 2) || W8A8_MID(4, 2, 4, 3) ||
+        W8A8_MID(4, 1, 4, 3) || W8A8_MID(4, 4, 4, 2);
 #undef W8A8_MID
+    if (!launched) return hipErrorInvalidValue;
   } else if (M <= kSkinnyMaxM) {
 #define W8A8_SKINNY(MTV, RWV, NWV, UV, LATEV)                                            \
   launch_skinny<MTV, RWV, NWV, UV, I32OUT, LATEV>(xq, ldq, s_tok, wq, ldw, s_chan, M, N, K, y, \
