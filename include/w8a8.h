@@ -20,7 +20,8 @@
  *   - Every call is enqueued on `stream` (0 = the null stream) and returns
  *     before the GPU work completes. The caller owns all memory; inputs and
  *     outputs must stay valid until the stream reaches the call. The library
- *     never allocates device memory and keeps no state between calls.
+ *     never allocates device memory; the only state it keeps between calls
+ *     is each device's compute-unit count, read once for tile choices.
  *   - Arguments are validated on the host before any HIP call. A failed
  *     check returns an error status and enqueues nothing. Device faults
  *     surface at the caller's next synchronization, as for any HIP kernel.
