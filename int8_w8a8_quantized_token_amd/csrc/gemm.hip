@@ -565,8 +565,10 @@ __device__ __forceinline__ void prefill_tile_coords(int t_lin, int tiles_n, int 
 // ks + 1's LDS reads go out while k-step ks multiplies.
 //
 // Schedule inside a stage. LDS serves both the fragment reads (192 KB per
-// stage per CU) and the DMA writes (64 KB), about 84% of its bandwidth at
-// the full MFMA rate, so bursts stall the matrix cores. Two things spread
+// stage per CU) and the DMA writes (64 KB); at the full MFMA rate (2048
+// cycles per stage) the reads alone need 96 B/clk, about three quarters of
+// what a read-only loop reaches on MI355X, so bursts stall the matrix
+// cores. Two things spread
 // the load: each k-step's reads are interleaved one-for-one with its MFMAs
 // (scheduling group barriers), and the next stage's DMA goes out in two
 // halves, one right after the barrier and one after k-step 0's MFMAs.
