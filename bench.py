@@ -63,9 +63,9 @@ def log(*a):
 # GEMM sources and the headers they include, comments and blank lines
 # removed) only; for any other code the field is null.
 MEASURED_TRAFFIC = {
-    "gemm_code_sha256": "9ff7b2e49c608bc1e309dcfb26cb84837d83a67c284e2a08b68ff26e9374bf10",
-    "decode": 56274826,
-    "prefill": 427692262,
+    "gemm_code_sha256": "95bc7ca3ba832f11e7adbf2361ef994f87e348290ae2cda7ea17462d76d21e67",
+    "decode": 56277083,
+    "prefill": 427699268,
 }
 GEMM_SRCS = [os.path.join("int8_w8a8_quantized_token_amd", "csrc", f)
              for f in ("gemm.hip", "gemm_common.h", "gemm_dispatch.h", "device_common.h")]

@@ -988,8 +988,6 @@ static void launch_prefill(const int8_t* xq, int64_t ldq, const float* s_tok, co
 // Dispatch
 // ---------------------------------------------------------------------------
 
-using dispatch::kSkinnyMaxM;
-constexpr int kPrefillMinM = 512;
 
 template <int MT, int RW, int NW, int U, bool I32OUT, bool LATE = false>
 static void launch_skinny(const int8_t* xq, int64_t ldq, const float* s_tok, const int8_t* wq,
@@ -1012,6 +1010,18 @@ static void launch_mid(const int8_t* xq, int64_t ldq, const float* s_tok, const 
                      wq, ldw, s_chan, M, N, K, y, ldy, c, ldc, vec_out, rot);
 }
 
+// One register-staged decode-kernel instance if its arguments are the chosen ones.
+template <int MT, int RW, int NW, int U, bool LATE, bool I32OUT>
+static bool launch_skinny_if(const dispatch::SkinnyConfig& k, const int8_t* xq, int64_t ldq,
+                             const float* s_tok, const int8_t* wq, int64_t ldw,
+                             const float* s_chan, int M, int N, int K, uint16_t* y, int64_t ldy,
+                             int32_t* c, int64_t ldc, bool vec_out, hipStream_t s) {
+  if (k.mt != MT || k.rw != RW || k.nw != NW || k.u != U || k.late != LATE) return false;
+  launch_skinny<MT, RW, NW, U, I32OUT, LATE>(xq, ldq, s_tok, wq, ldw, s_chan, M, N, K, y, ldy, c,
+                                              ldc, vec_out, s);
+  return true;
+}
+
 // One decode-kernel instance if its template arguments are the chosen ones.
 template <int MT, int RW, int NW, int NS, bool I32OUT>
 static bool launch_mid_if(const dispatch::MidConfig& m, const int8_t* xq, int64_t ldq,
@@ -1029,7 +1039,8 @@ static hipError_t launch_gemm_t(const int8_t* xq, int64_t ldq, const float* s_to
                                 const int8_t* wq, int64_t ldw, const float* s_chan, int M,
                                 int N, int K, uint16_t* y, int64_t ldy, int32_t* c, int64_t ldc,
                                 bool vec_out, hipStream_t s) {
-  if (dispatch::mid_path(M, N, K)) {
+  const dispatch::GemmPath path = dispatch::gemm_path(M, N, K);
+  if (path == dispatch::GemmPath::kMid) {
     // Every configuration dispatch::mid_config can return has an instance.
     const dispatch::MidConfig m = dispatch::mid_config(M, N, K, device_cus());
 #define W8A8_MID(MTV, RWV, NWV, NSV)                                                       \
@@ -1043,44 +1054,27 @@ static hipError_t launch_gemm_t(const int8_t* xq, int64_t ldq, const float* s_to
         W8A8_MID(4, 1, 4, 3) || W8A8_MID(4, 4, 4, 2);
 #undef W8A8_MID
     if (!launched) return hipErrorInvalidValue;
-  } else if (M <= kSkinnyMaxM) {
-#define W8A8_SKINNY(MTV, RWV, NWV, UV, LATEV)                                            \
-  launch_skinny<MTV, RWV, NWV, UV, I32OUT, LATEV>(xq, ldq, s_tok, wq, ldw, s_chan, M, N, K, y, \
-                                                  ldy, c, ldc, vec_out, s)
-    // Shape classes measured on MI355X (Llama-3.1-8B projection shapes). More
-    // weight rows per wave (RW) reuse each token fragment more often but
-    // leave fewer workgroups; they pay off once N is large or M > 16. Late
-    // scale loads (last argument) where the scales held through the weight
-    // stream would cost a wave per SIMD.
-    const bool wide = N > 8192, mid = N > 4096 && N <= 8192, deep = K > 8192;
-    if (M <= 4) {
-      if (mid) W8A8_SKINNY(1, 2, 8, 8, false);
-      else if (wide || deep) W8A8_SKINNY(1, 1, 16, 2, false);
-      else W8A8_SKINNY(1, 1, 16, 8, false);
-    } else if (M <= 16) {
-      if (wide) W8A8_SKINNY(1, 4, 8, 2, false);
-      else if (mid) W8A8_SKINNY(1, 2, 8, 8, true);
-      else if (deep) W8A8_SKINNY(1, 1, 8, 4, false);
-      else W8A8_SKINNY(1, 1, 16, 8, false);
-    } else if (M <= 32) {
-      if (wide) W8A8_SKINNY(2, 4, 4, 2, true);
-      else if (mid) W8A8_SKINNY(2, 2, 8, 4, false);
-      else W8A8_SKINNY(2, 1, 16, 4, false);
-    } else if (M <= 48) {
-      if (wide) W8A8_SKINNY(3, 4, 4, 2, false);
-      else if (mid) W8A8_SKINNY(3, 2, 8, 2, false);
-      else W8A8_SKINNY(3, 1, 16, 2, false);
-    } else {
-      if (wide) W8A8_SKINNY(4, 4, 4, 2, true);
-      else if (mid) W8A8_SKINNY(4, 2, 8, 2, false);
-      else if (deep) W8A8_SKINNY(4, 1, 16, 2, false);
-      else W8A8_SKINNY(4, 1, 8, 8, false);
-    }
+  } else if (path == dispatch::GemmPath::kSkinny) {
+    // Every configuration dispatch::skinny_config can return has an instance.
+    const dispatch::SkinnyConfig k = dispatch::skinny_config(M, N, K);
+#define W8A8_SKINNY(MTV, RWV, NWV, UV, LATEV)                                                     \
+  launch_skinny_if<MTV, RWV, NWV, UV, LATEV, I32OUT>(k, xq, ldq, s_tok, wq, ldw, s_chan, M, N, K, \
+                                                     y, ldy, c, ldc, vec_out, s)
+    const bool launched =
+        W8A8_SKINNY(1, 2, 8, 8, false) || W8A8_SKINNY(1, 1, 16, 2, false) ||
+        W8A8_SKINNY(1, 1, 16, 8, false) || W8A8_SKINNY(1, 4, 8, 2, false) ||
+        W8A8_SKINNY(1, 2, 8, 8, true) || W8A8_SKINNY(1, 1, 8, 4, false) ||
+        W8A8_SKINNY(2, 4, 4, 2, true) || W8A8_SKINNY(2, 2, 8, 4, false) ||
+        W8A8_SKINNY(2, 1, 16, 4, false) || W8A8_SKINNY(3, 4, 4, 2, false) ||
+        W8A8_SKINNY(3, 2, 8, 2, false) || W8A8_SKINNY(3, 1, 16, 2, false) ||
+        W8A8_SKINNY(4, 4, 4, 2, true) || W8A8_SKINNY(4, 2, 8, 2, false) ||
+        W8A8_SKINNY(4, 1, 16, 2, false) || W8A8_SKINNY(4, 1, 8, 8, false);
 #undef W8A8_SKINNY
-  } else if (K % pf128::BK == 0) {
+    if (!launched) return hipErrorInvalidValue;
+  } else if (path == dispatch::GemmPath::kPrefill128) {
     launch_prefill128_auto<I32OUT>(xq, ldq, s_tok, wq, ldw, s_chan, M, N, K, y, ldy, c, ldc,
                                    vec_out, s);
-  } else if (M >= kPrefillMinM) {
+  } else if (path == dispatch::GemmPath::kPrefill64) {
     launch_prefill<2, 4, I32OUT>(xq, ldq, s_tok, wq, ldw, s_chan, M, N, K, y, ldy, c, ldc, vec_out,
                                  s);
   } else {

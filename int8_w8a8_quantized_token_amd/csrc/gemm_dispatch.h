@@ -1,7 +1,6 @@
 // Host-side choice of the GEMM kernel and its tile from the problem shape
-// and the device's CU count, for K % 128 == 0 (the LDS-staged decode kernel
-// and the full-line prefill kernel). Plain C++, no HIP types, so the rules
-// also compile and can be checked on a host without a GPU; the launchers in
+// and the device's CU count. Plain C++, no HIP types, so the rules also
+// compile and can be checked on a host without a GPU; the launchers in
 // gemm.hip map each answer onto a template instance.
 
 #pragma once
@@ -12,7 +11,8 @@ namespace w8a8 {
 namespace dispatch {
 
 constexpr int kMidBK = 128;       // K bytes per stage of the LDS-staged kernels
-constexpr int kSkinnyMaxM = 64;   // one M tile of the decode kernel covers the tokens
+constexpr int kSkinnyMaxM = 64;   // one M tile of the decode kernels covers the tokens
+constexpr int kPrefillMinM = 512; // other K: the 64-byte-stage prefill kernel from here
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -26,6 +26,21 @@ inline bool mid_path(int64_t M, int64_t N, int64_t K) {
   if (M <= kSkinnyMaxM) return true;
   if (N >= 16384) return M <= 128;
   return M <= (K > 8192 ? 1536 : 1024);
+}
+
+enum class GemmPath {
+  kMid,         // LDS-staged decode kernel, K % 128 == 0 (also M-tiled past 64)
+  kSkinny,      // register-staged decode kernel, other K, M <= 64
+  kPrefill128,  // full-line prefill kernel, K % 128 == 0
+  kPrefill64,   // 64-byte-stage prefill kernel, other K, M >= 512
+  kTiled,       // register-staged 128 x 128 tiles, other K, 64 < M < 512
+};
+
+inline GemmPath gemm_path(int64_t M, int64_t N, int64_t K) {
+  if (mid_path(M, N, K)) return GemmPath::kMid;
+  if (M <= kSkinnyMaxM) return GemmPath::kSkinny;
+  if (K % kMidBK == 0) return GemmPath::kPrefill128;
+  return M >= kPrefillMinM ? GemmPath::kPrefill64 : GemmPath::kTiled;
 }
 
 // Template arguments of the decode kernel: 16 * mt token rows and 16 * rw
@@ -90,6 +105,48 @@ inline MidConfig mid_config(int64_t M, int64_t N, int64_t K, int64_t cus) {
   const int64_t groups = cdiv(N, 64) * cdiv(M, 64);
   if (2 * cdiv(groups, cus) <= 3 * cdiv(groups, 2 * cus)) return {4, 4, 4, 2};
   return {4, 4, 2, 2};
+}
+
+// Template arguments of the register-staged decode kernel (K % 128 != 0):
+// up to 16 * mt tokens and 16 * rw output channels per workgroup, nw waves,
+// u 64-byte K chunks in flight per wave, and late scale loads.
+struct SkinnyConfig {
+  int mt, rw, nw, u;
+  bool late;
+};
+
+// Shape classes measured on MI355X (Llama-3.1-8B projection shapes). More
+// weight rows per wave (RW) reuse each token fragment more often but leave
+// fewer workgroups; they pay off once N is large or M > 16. The scales load
+// after the weight stream (late) where holding them through it would cost
+// a wave per SIMD.
+inline SkinnyConfig skinny_config(int64_t M, int64_t N, int64_t K) {
+  const bool wide = N > 8192, mid = N > 4096 && N <= 8192, deep = K > 8192;
+  if (M <= 4) {
+    if (mid) return {1, 2, 8, 8, false};
+    if (wide || deep) return {1, 1, 16, 2, false};
+    return {1, 1, 16, 8, false};
+  }
+  if (M <= 16) {
+    if (wide) return {1, 4, 8, 2, false};
+    if (mid) return {1, 2, 8, 8, true};
+    if (deep) return {1, 1, 8, 4, false};
+    return {1, 1, 16, 8, false};
+  }
+  if (M <= 32) {
+    if (wide) return {2, 4, 4, 2, true};
+    if (mid) return {2, 2, 8, 4, false};
+    return {2, 1, 16, 4, false};
+  }
+  if (M <= 48) {
+    if (wide) return {3, 4, 4, 2, false};
+    if (mid) return {3, 2, 8, 2, false};
+    return {3, 1, 16, 2, false};
+  }
+  if (wide) return {4, 4, 4, 2, true};
+  if (mid) return {4, 2, 8, 2, false};
+  if (deep) return {4, 1, 16, 2, false};
+  return {4, 1, 8, 8, false};
 }
 
 // Tile of the full-line prefill kernel, weight rows x tokens (measured on

@@ -28,7 +28,8 @@ def pick(tmp_path_factory):
         res = []
         for ln in lines:
             f = ln.split()
-            res.append(("mid",) + tuple(int(v) for v in f[1:]) if f[0] == "mid" else tuple(f))
+            res.append((f[0],) + tuple(int(v) for v in f[1:]) if f[0] in ("mid", "skinny")
+                       else tuple(f))
         return res
     return run
 
@@ -82,7 +83,7 @@ def test_decode_and_prefill_limits(pick):
     assert got[1][0] == "prefill"
     assert got[2][0] == "mid" and got[3][0] == "prefill"
     assert got[4][0] == "mid" and got[5][0] == "prefill"
-    assert got[6] == ("other",) and got[7] == ("other",)      # K % 128 != 0
+    assert got[6][0] == "skinny" and got[7] == ("tiled",)     # K % 128 != 0
 
 
 def test_m_tiled_waves_by_rounds(pick):
@@ -121,3 +122,30 @@ def test_rules_follow_the_cu_count(pick):
     assert got[0] == ("mid", 1, 1, 4, 3)
     assert got[1] == ("prefill", "256x256")
     assert got[2] == ("prefill", "256x256")
+
+
+def test_other_k_routes_and_skinny_classes(pick):
+    # K % 128 != 0: the register-staged decode kernel up to 64 tokens, the
+    # 128 x 128 tiles below 512 and the 64-byte-stage prefill kernel above;
+    # the decode classes by N (wide > 8192, mid 4096..8192), K (deep > 8192)
+    # and token count, with late scale loads where the table says so
+    cases = {
+        (1, 6144, 4112): ("skinny", 1, 2, 8, 8, 0),
+        (4, 28672, 4112): ("skinny", 1, 1, 16, 2, 0),
+        (1, 4096, 14352): ("skinny", 1, 1, 16, 2, 0),
+        (3, 4096, 4112): ("skinny", 1, 1, 16, 8, 0),
+        (16, 28672, 4112): ("skinny", 1, 4, 8, 2, 0),
+        (16, 6144, 4112): ("skinny", 1, 2, 8, 8, 1),
+        (16, 4096, 14352): ("skinny", 1, 1, 8, 4, 0),
+        (32, 28672, 4112): ("skinny", 2, 4, 4, 2, 1),
+        (48, 6144, 4112): ("skinny", 3, 2, 8, 2, 0),
+        (64, 28672, 4112): ("skinny", 4, 4, 4, 2, 1),
+        (64, 4096, 14352): ("skinny", 4, 1, 16, 2, 0),
+        (64, 4096, 4112): ("skinny", 4, 1, 8, 8, 0),
+        (65, 4096, 4112): ("tiled",),
+        (511, 4096, 4112): ("tiled",),
+        (512, 4096, 4112): ("prefill64",),
+    }
+    got = pick([k + (CUS,) for k in cases])
+    assert got == list(cases.values())
+
