@@ -14,10 +14,20 @@ seeded synthetic bf16 inputs with 1% outlier channels x20.
     M = 4096. Metric: int8 TOPS = 2MNK per linear / time.
 
 Each step is captured once in a HIP graph and replayed; W untimed warmup
-steps, then K timed steps between two events on the replay stream.
+steps, then K timed steps between two events on the replay stream (one
+more event after each replay gives the median, 95th percentile and mean).
 The roofline entry times the dominant kernel (the GEMM) alone: a graph of
 the step's GEMM launches only, timed the same way; its average launch
 duration is the graph time over the number of launches.
+
+Also reported: the same decode step with one calibrated activation scale
+per projection (static_decode); a 32-layer block chain at 3000 tokens with
+the fused norm and SiLU producers (chain); the Llama-3-70B projections at
+32 and 2048 tokens (llama70b); the cost of a kernel boundary in a graph
+(dispatch_floor_us); the shader and memory clocks before and after; and
+the CPU oracle on a bounded sample (cpu_baseline). --detail adds per-shape
+times of the linear, the GEMM alone and the quantizer alone; --counters
+only launches every GEMM once for hardware-counter passes.
 """
 import argparse
 import json
