@@ -20,9 +20,11 @@ The roofline entry times the dominant kernel (the GEMM) alone: a graph of
 the step's GEMM launches only, timed the same way; its average launch
 duration is the graph time over the number of launches.
 
-Also reported: the same decode step with one calibrated activation scale
-per projection (static_decode); a 32-layer block chain at 3000 tokens with
-the fused norm and SiLU producers (chain); the Llama-3-70B projections at
+Also reported: the decode step split by token count (decode_by_m, whole
+linear and GEMM alone against the HBM peak); the same decode step with one
+calibrated activation scale per projection (static_decode); a 32-layer
+block chain at 3000 tokens with the fused norm and SiLU producers (chain);
+the Llama-3-70B projections at
 32 and 2048 tokens (llama70b); the cost of a kernel boundary in a graph
 (dispatch_floor_us); the shader and memory clocks before and after; and
 the CPU oracle on a bounded sample (cpu_baseline). --detail adds per-shape
@@ -554,6 +556,19 @@ def main():
     }
     if d_per:
         out["per_shape_decode"] = d_per
+
+    # the same step split by token count: the four projections x 32 layers
+    # at one M, whole linear and GEMM alone, against the HBM peak
+    by_m = {}
+    for M in DECODE_MS:
+        m_step, m_gemm, _, _, _ = run_phase(torch, S, (M,), args.steps, args.warmup, False)
+        lb = sum(lin_bytes(M, N, K) for _, N, K in S.shapes) * LAYERS
+        gb = sum(gemm_bytes(M, N, K) for _, N, K in S.shapes) * LAYERS
+        lin, gem = lb / (m_step * 1e-3) / 1e9, gb / (m_gemm * 1e-3) / 1e9
+        by_m[str(M)] = {"linear_GBps": round(lin, 1), "linear_frac": round(lin / HBM_PEAK_GBS, 4),
+                        "gemm_GBps": round(gem, 1), "gemm_frac": round(gem / HBM_PEAK_GBS, 4)}
+    out["decode_by_m"] = by_m
+    log(f"[bench] decode by token count: {by_m}")
 
     # the same decode step with the static (calibrated, per-tensor) activation scale
     def static_step():
