@@ -442,10 +442,11 @@ def linear_static(x_bf16: np.ndarray, smooth, scale, wq: np.ndarray, s_chan: np.
 # factor is computed" folds the smoothing division into that weight. A
 # producer that ends in the quantizer therefore emits int8 codes and per-token
 # scales directly. Readings where the pages say nothing:
-#   * RMSNorm: ms = mean of h^2 over the row, the exact sum rounded once to
-#     binary32; inv = 1 / sqrt(ms + eps), each step one binary32 rounding
-#     (sum, square root, division); y = (h * inv) * g with g = gamma / s
-#     folded once per channel (binary32); then per-token quantization of y;
+#   * RMSNorm: ms = mean of h^2 over the row: the exact sum divided by K
+#     and rounded once to binary32; inv = 1 / sqrt(ms + eps), each step one
+#     binary32 rounding (sum, square root, division); y = (h * inv) * g with
+#     g = gamma / s folded once per channel (binary32); then per-token
+#     quantization of y;
 #   * residual add: h = bf16(h + r), the binary32 sum of two bf16 values
 #     rounded to bf16 (it becomes the new residual stream);
 #   * SiLU-gated product: m = bf16((g / (1 + exp(-g))) * u) evaluated in
@@ -468,13 +469,55 @@ def residual_add(h_bf16: np.ndarray, r_bf16: np.ndarray) -> np.ndarray:
     return round_to_bf16(bf16_to_f32(h_bf16) + bf16_to_f32(r_bf16))
 
 
+def _bf16_square_sum_scaled(row_bits) -> int:
+    """The exact sum of the squares of a row of bf16 values, times 2^266,
+    as a Python integer.
+
+    A bf16 value with biased exponent E and fraction f is m 2^(e) with the
+    integer significand m = f (E = 0) or 128 + f, and e = max(E, 1) - 134,
+    so e >= -133 and its square m^2 2^(2e) is an integer multiple of 2^-266.
+    """
+    b = np.asarray(row_bits, dtype=np.uint16).astype(np.int64)
+    E = (b >> 7) & 0xFF
+    f = b & 0x7F
+    m = np.where(E == 0, f, f | 0x80)
+    k = np.maximum(E, 1) - 1                     # e + 133, 0 .. 253
+    total = 0
+    for kk, mm in zip(k.tolist(), m.tolist()):
+        total += (mm * mm) << (2 * kk)
+    return total
+
+
+def _round_ratio_f32(num: int, den: int) -> np.float32:
+    """num / den (integers, num >= 0, den > 0) rounded once to binary32,
+    nearest with ties to even, with subnormals and overflow to +inf."""
+    if num == 0:
+        return F32(0)
+    e = num.bit_length() - den.bit_length()      # 2^(e-1) < num/den < 2^(e+1)
+    if (num << max(-e, 0)) < (den << max(e, 0)):
+        e -= 1                                   # now 2^e <= num/den < 2^(e+1)
+    qe = max(e - 23, -149)                       # exponent of the last kept bit
+    if qe >= 0:
+        n, r = divmod(num, den << qe)
+        half = den << qe
+    else:
+        n, r = divmod(num << -qe, den)
+        half = den
+    if 2 * r > half or (2 * r == half and n % 2 == 1):
+        n += 1
+    if e >= 128 or n * 2.0 ** qe >= 2.0 ** 128:
+        return F32(np.inf)
+    return F32(np.ldexp(float(n), qe))           # n < 2^25: exact in both formats
+
+
 def rms_inverse(h_bf16: np.ndarray, eps) -> np.ndarray:
-    """inv[m] = RN32(1 / RN32(sqrt(RN32(ms[m] + eps)))), ms the mean of squares
-    of the row (exact sum, one rounding to binary32)."""
-    import math
-    h = bf16_to_f32(h_bf16).astype(np.float64)
+    """inv[m] = RN32(1 / RN32(sqrt(RN32(ms[m] + eps)))) with ms[m] the mean of
+    the squares of row m: the exact sum divided by K, rounded once to
+    binary32 (no intermediate rounding of the sum or of the quotient)."""
+    h = np.asarray(h_bf16, dtype=np.uint16)
     K = h.shape[1]
-    ms = np.array([math.fsum((row * row).tolist()) / K for row in h]).astype(F32)
+    ms = np.array([_round_ratio_f32(_bf16_square_sum_scaled(row), K << 266) for row in h],
+                  dtype=F32)
     d = (ms + F32(eps)).astype(F32)
     return (F32(1) / np.sqrt(d).astype(F32)).astype(F32)
 

@@ -164,6 +164,44 @@ def _fold_gamma_multiplies(gamma, smooth):
     return g.copy() if smooth is None else (g * np.asarray(smooth, F32)).astype(F32)
 
 
+def _rms_double_rounding(h_bf16, eps):          # sum rounded to binary64, then /K, then binary32
+    import math
+    h = O.bf16_to_f32(h_bf16).astype(np.float64)
+    ms = np.array([math.fsum((row * row).tolist()) / h.shape[1] for row in h]).astype(F32)
+    return (F32(1) / np.sqrt((ms + F32(eps)).astype(F32)).astype(F32)).astype(F32)
+
+
+def _silu_quantize_drops_smooth(gu_bf16, smooth):
+    return O.quantize_act(O.silu_mul(gu_bf16), None)
+
+
+def _chain_variant(qkv_slice=0, final_residual=True):
+    # the block chain with one wiring mistake: o reads another K-column slice
+    # of the qkv output, or the last residual add is left out
+    def chain(x_bf16, layers, eps=1e-5):
+        h = np.asarray(x_bf16, dtype=np.uint16)
+        K = h.shape[1]
+        pending = None
+
+        def lin(q, S, w):
+            return O.dequant_epilogue(O.gemm_i32(q, w[0]), S, w[1])[1]
+
+        for L in layers:
+            q, S, h = O.rmsnorm_quantize(h, pending, L["g_attn"], eps)
+            y_qkv = lin(q, S, L["qkv"])
+            c0 = qkv_slice * K
+            q, S = O.quantize_act(np.ascontiguousarray(y_qkv[:, c0:c0 + K]), L["s_o"])
+            y_o = lin(q, S, L["o"])
+            q, S, h = O.rmsnorm_quantize(h, y_o, L["g_mlp"], eps)
+            y_gu = lin(q, S, L["gate_up"])
+            q, S = O.silu_mul_quantize(y_gu, L["s_down"])
+            pending = lin(q, S, L["down"])
+        if pending is None:
+            return h
+        return O.residual_add(h, pending) if final_residual else pending
+    return chain
+
+
 _real_rmsnorm_quantize = O.rmsnorm_quantize
 
 
@@ -230,6 +268,11 @@ MUTANTS = {
     "static_uses_token_scale": ("quantize_act_static_f32", _static_uses_token_scale),
     "rms_sum_not_mean": ("rms_inverse", _rms_sum_not_mean),
     "rms_eps_outside_sqrt": ("rms_inverse", _rms_eps_outside),
+    "rms_mean_rounded_twice": ("rms_inverse", _rms_double_rounding),
+    "silu_quantize_drops_smoothing": ("silu_mul_quantize", _silu_quantize_drops_smooth),
+    "chain_o_reads_k_slice": ("chain_forward", _chain_variant(qkv_slice=1)),
+    "chain_o_reads_v_slice": ("chain_forward", _chain_variant(qkv_slice=2)),
+    "chain_drops_last_residual": ("chain_forward", _chain_variant(final_residual=False)),
     "fold_gamma_multiplies": ("fold_gamma", _fold_gamma_multiplies),
     "rmsnorm_drops_residual": ("rmsnorm_quantize", _rmsnorm_drops_residual),
     "silu_halves_swapped": ("silu_mul", _silu_halves_swapped),

@@ -9,6 +9,7 @@ or bf16 rounding in the oracle fails at least one of them.
 import json
 import math
 import os
+import struct
 from decimal import Decimal, getcontext
 from fractions import Fraction
 
@@ -615,6 +616,34 @@ def test_rms_inverse_vs_fraction():
         assert Fraction(float(inv[m])) == _rms_inv_exact(row, 1e-5)
 
 
+def test_rms_inverse_rounds_the_mean_once():
+    # 2.421875^2 + 0.05615234375^2 = 24614825 / 2^22 is exact in binary64, and
+    # a sixteenth of it lies exactly halfway between two binary32 values. A
+    # tiny entry (2^-60, square 2^-120; or bf16's least subnormal 2^-133,
+    # square 2^-266) puts the exact mean just above that midpoint: one
+    # rounding of the exact mean goes up, while rounding the sum to binary64
+    # first loses the tiny square and the tie then goes to even (down).
+    # Without a tiny entry the mean is the tie itself.
+    K = 16
+    tie = Fraction(24614825, 2 ** 22) / K
+    assert rn32(tie) != rn32(tie + Fraction(1, 2 ** 300))
+    rows = np.zeros((4, K), F32)
+    rows[:, :2] = [2.421875, 0.05615234375]
+    rows[0, 2] = 2.0 ** -60
+    rows[2, 15] = -(2.0 ** -133)
+    rows[3, 0] = -2.421875                     # signs do not matter
+    rows[3, 9] = 2.0 ** -60
+    h = O.round_to_bf16(rows)
+    assert np.array_equal(O.bf16_to_f32(h), rows)
+    for eps in (1e-5, 0.0):
+        inv = O.rms_inverse(h, eps)
+        for m in range(4):
+            assert Fraction(float(inv[m])) == _rms_inv_exact(rows[m].tolist(), eps), (m, eps)
+        assert inv[0] == inv[2] == inv[3]
+    inv = O.rms_inverse(h, 1e-5)
+    assert inv[0] < inv[1]                     # the larger mean, the smaller inverse
+
+
 def test_rmsnorm_quantize_vs_fraction():
     r = np.random.default_rng(21)
     K = 48
@@ -680,6 +709,98 @@ def test_silu_mul_vs_high_precision():
     # gate and up are the two halves in that order: a zero gate zeroes the product
     gu2 = O.round_to_bf16(np.concatenate([np.zeros((1, 8), F32), np.full((1, 8), 7, F32)], 1))
     assert np.all(O.bf16_to_f32(O.silu_mul(gu2)) == 0)
+
+
+def _bf16_float(bits: int) -> float:
+    return struct.unpack("<f", struct.pack("<I", (bits & 0xFFFF) << 16))[0]
+
+
+def test_silu_mul_quantize_vs_high_precision():
+    # the producer's codes from the SiLU product of 80-digit decimals, the
+    # smoothing division and the per-token quantizer, all rounded exactly
+    r = np.random.default_rng(25)
+    inter = 24
+    gate = r.standard_normal((2, inter)) * 3
+    up = r.standard_normal((2, inter))
+    gu = O.round_to_bf16(np.concatenate([gate, up], axis=1).astype(F32))
+    s = np.exp(r.uniform(-1.5, 1.5, inter)).astype(F32)
+    q, S = O.silu_mul_quantize(gu, s)
+    x = O.bf16_to_f32(gu)
+    for i in range(2):
+        m = [_bf16_float(_silu_mul_exact(x[i, j], x[i, inter + j])) for j in range(inter)]
+        qr, Sr = ref_quantize_row(m, s)
+        assert q[i].tolist() == qr
+        assert Fraction(float(S[i])) == Sr
+
+
+def _ref_linear_row(q, S, wq, sw):
+    """One token row through the integer GEMM and the binary32 epilogue,
+    with Python integers and exact rationals."""
+    out = []
+    for n in range(wq.shape[0]):
+        acc = sum(int(a) * int(b) for a, b in zip(q, wq[n]))
+        out.append(rnbf16(rn32(rn32(rn32(Fraction(acc)) * S) * Fraction(float(sw[n])))))
+    return out
+
+
+def _ref_rmsnorm_row(h, res, g, eps):
+    """(residual add,) RMSNorm and the per-token quantizer on one row of exact
+    bf16 values; returns (codes, scale, new residual stream)."""
+    if res is not None:
+        h = [rnbf16(rn32(a + b)) for a, b in zip(h, res)]
+    inv = _rms_inv_exact([float(v) for v in h], eps)
+    y = [rn32(rn32(v * inv) * Fraction(float(gk))) for v, gk in zip(h, g)]
+    a = max(abs(v) for v in y)
+    S = rn32(a / 127)
+    q = [0] * len(y) if S == 0 else [max(-127, min(127, half_away(rn32(v / S)))) for v in y]
+    return q, S, h
+
+
+def _ref_chain_row(x, layers, K, inter, eps=1e-5):
+    """The block chain on one token, every step with exact arithmetic: pre-
+    norm, qkv, the first K columns of qkv through o, residual + norm,
+    gate_up, SiLU of the first half times the second, down, residual."""
+    h = [Fraction(float(v)) for v in x]
+    pending = None
+    for L in layers:
+        q, S, h = _ref_rmsnorm_row(h, pending, L["g_attn"], eps)
+        y_qkv = _ref_linear_row(q, S, *L["qkv"])
+        q, S = ref_quantize_row([float(v) for v in y_qkv[:K]], L["s_o"])
+        y_o = _ref_linear_row(q, S, *L["o"])
+        q, S, h = _ref_rmsnorm_row(h, y_o, L["g_mlp"], eps)
+        y_gu = _ref_linear_row(q, S, *L["gate_up"])
+        m = [_bf16_float(_silu_mul_exact(float(y_gu[j]), float(y_gu[inter + j])))
+             for j in range(inter)]
+        q, S = ref_quantize_row(m, L["s_down"])
+        pending = _ref_linear_row(q, S, *L["down"])
+    return [rnbf16(rn32(a + b)) for a, b in zip(h, pending)]
+
+
+def test_chain_forward_vs_exact_arithmetic():
+    # two small layers with smoothing factors and an outlier gamma, checked
+    # row by row against the chain rebuilt from exact rationals
+    r = np.random.default_rng(26)
+    K, inter = 16, 24
+    def lw(n, k):
+        w = O.round_to_bf16(r.standard_normal((n, k)).astype(F32) * F32(0.2))
+        return O.quantize_weight(w)
+    layers = []
+    for _ in range(2):
+        gamma = np.ones(K, F32)
+        gamma[[2, 11]] = 20.0
+        layers.append({
+            "g_attn": O.fold_gamma(gamma, np.exp(r.uniform(-1, 1, K)).astype(F32)),
+            "g_mlp": np.exp(r.uniform(-0.5, 0.5, K)).astype(F32),
+            "s_o": np.exp(r.uniform(-1, 1, K)).astype(F32),
+            "s_down": np.exp(r.uniform(-1, 1, inter)).astype(F32),
+            "qkv": lw(3 * K, K), "o": lw(K, K), "gate_up": lw(2 * inter, K),
+            "down": lw(K, inter)})
+    x = O.round_to_bf16(r.standard_normal((2, K)).astype(F32))
+    out = O.chain_forward(x, layers)
+    xf = O.bf16_to_f32(x)
+    for m in range(2):
+        ref = _ref_chain_row(xf[m], layers, K, inter)
+        assert out[m].tolist() == [bf16_bits_of(v) for v in ref], m
 
 
 def test_chain_rows_are_independent():
