@@ -280,7 +280,7 @@ w8a8_status_t w8a8_calibrate_entropy(const uint32_t* hist, int64_t bins, const f
 /*
  * Optional residual add, RMSNorm with a folded weight, per-token quantization:
  *   if residual: h[m,k] = bf16(h[m,k] + residual[m,k])   (binary32 sum; h written)
- *   ms[m]  = sum_k h[m,k]^2 / K, the exact sum rounded once to binary32
+ *   ms[m]  = sum_k h[m,k]^2 / K: the exact mean, rounded once to binary32
  *   inv[m] = 1 / sqrt(ms[m] + eps)                         (binary32 steps)
  *   y[m,k] = (h[m,k] * inv[m]) * gamma[k]                  (binary32)
  *   s_tok[m] = max_k |y[m,k]| / 127; xq = clamp(round(y / s_tok), -127, 127)

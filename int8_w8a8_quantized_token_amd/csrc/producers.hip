@@ -8,7 +8,8 @@
 // tensors") and folds the SmoothQuant division into that weight (section
 // "How the SmoothQuant smoothing factor is computed"). So:
 //   * add + RMSNorm + quantize: h = bf16(h + r) (optional, written back as the
-//     new residual stream); ms = sum(h^2) / K rounded once to binary32;
+//     new residual stream); ms = sum(h^2) / K, the exact mean rounded once
+//     to binary32;
 //     inv = 1 / sqrt(ms + eps); y = (h * inv) * g with g = gamma / s; then
 //     S = max|y| / 127 and codes;
 //   * SiLU-gated product + quantize: m = bf16((g / (1 + exp(-g))) * u), the
@@ -17,8 +18,9 @@
 //     bf16 gate and up halves of a row; x' = m / s; codes.
 //
 // The sum of squares is exact per term (a bf16 square fits binary64) and is
-// accumulated with error-free transformations (two-sum, double-double), so
-// the rounded result does not depend on the summation order.
+// accumulated in double-double; the binary32 rounding of the mean is then
+// decided exactly (mean_square_rn32), so it does not depend on the order of
+// the sum.
 
 #include "device_common.h"
 #include "launchers.h"
@@ -65,9 +67,10 @@ __device__ __forceinline__ DD dd_shfl_xor(DD x, int off) {
   return r;
 }
 
-// Block-wide double-double sum; every thread gets hi + lo.
+// Block-wide double-double sum (normalized: |lo| <= ulp(hi) / 2); every
+// thread gets the same value.
 template <int BS>
-__device__ __forceinline__ double block_sum_dd(DD v, DD* red) {
+__device__ __forceinline__ DD block_sum_dd(DD v, DD* red) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v = dd_add(v, dd_shfl_xor(v, off));
   const int wave = threadIdx.x / kWave;
@@ -76,7 +79,7 @@ __device__ __forceinline__ double block_sum_dd(DD v, DD* red) {
   DD t = red[0];
 #pragma unroll
   for (int w = 1; w < BS / kWave; ++w) t = dd_add(t, red[w]);
-  return t.hi + t.lo;
+  return t;
 }
 
 template <int BS>
@@ -116,6 +119,123 @@ __device__ __forceinline__ uint4 pack8_bf16(const float (&v)[8]) {
 }
 
 // ---------------------------------------------------------------------------
+// the mean of squares, rounded once to binary32
+// ---------------------------------------------------------------------------
+//
+// The row's sum of squares S arrives as a normalized double-double hi + lo.
+// Every term is nonnegative, the two-sum steps are exact and only the low
+// words' additions round (a thread adds at most 64 terms, then about 22
+// double-double additions combine the threads), so hi + lo is within 2^-90
+// of S, relatively. Its quotient by K, rounded to binary32, is therefore
+// RN32(S / K) or a binary32 neighbour of it; which one depends on the sign of
+// S - K t for the two midpoints t around that candidate. K t is exact in
+// binary64 (a midpoint has 25 significant bits, K < 2^17). Where
+// hi + lo - K t lies farther from 0 than 2^-70 hi, its sign is the sign of
+// S - K t; otherwise (the mean within 2^-70 of a midpoint, which real data
+// essentially never meets) the workgroup compares S and K t exactly.
+
+// Number of bins of exact_square_sum_cmp: a bf16 value with biased exponent E
+// is m 2^(e) with integer significand m < 256 and e = max(E, 1) - 134, so its
+// square is m^2 4^(max(E, 1) - 1) 2^-266 and squares fall into 254 bins.
+constexpr int kSqBins = 254;
+constexpr int kLimbs = 18;           // 32-bit limbs of S 2^266 < 2^539
+
+struct SqScratch {
+  unsigned long long bins[kSqBins];  // sum of m^2 per exponent (< 65536 * 2^16)
+  uint32_t s[kLimbs], t[kLimbs];     // S 2^266 and T 2^266, little-endian
+  int result;
+};
+
+// sign(S - T) for S the exact sum of squares of the row's values (v holds
+// bf16 values as floats; vectors vi = tid + i BS < nvec) and T > 0 a binary64
+// value with T 2^266 an integer. Called by every thread of the workgroup.
+template <int BS, int NV>
+__device__ __forceinline__ int exact_square_sum_cmp(const float (&v)[NV][8], int nvec, double T,
+                                                 SqScratch* sc) {
+  const int tid = threadIdx.x;
+  for (int k = tid; k < kSqBins; k += BS) sc->bins[k] = 0ull;
+  for (int k = tid; k < kLimbs; k += BS) { sc->s[k] = 0u; sc->t[k] = 0u; }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    if (tid + i * BS < nvec) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t b = __float_as_uint(v[i][e]) >> 16;   // the value's bf16 bits
+        const uint32_t E = (b >> 7) & 0xFFu, f = b & 0x7Fu;
+        const uint32_t m = E ? (f | 0x80u) : f;
+        if (m) atomicAdd(&sc->bins[E ? E - 1 : 0], (unsigned long long)(m * m));
+      }
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    // S 2^266 = sum_k bins[k] 4^k
+    for (int k = 0; k < kSqBins; ++k) {
+      unsigned long long add = sc->bins[k] << ((2 * k) & 31);   // < 2^63
+      for (int j = (2 * k) >> 5; add != 0ull && j < kLimbs; ++j) {
+        const unsigned long long cur = (unsigned long long)sc->s[j] + (add & 0xFFFFFFFFull);
+        sc->s[j] = (uint32_t)cur;
+        add = (add >> 32) + (cur >> 32);
+      }
+    }
+    // T 2^266 = mant 2^(ex + 266) for the normal binary64 T = mant 2^ex
+    const unsigned long long tb = (unsigned long long)__double_as_longlong(T);
+    const unsigned long long mant = (tb & 0xFFFFFFFFFFFFFull) | 0x10000000000000ull;
+    const int sh = (int)((tb >> 52) & 0x7FF) - 1075 + 266;            // >= 0 here
+    const int w = sh >> 5, b = sh & 31;
+    const unsigned long long lo = mant << b;                           // low 64 bits
+    const unsigned long long hi = b ? mant >> (64 - b) : 0ull;         // bits 64 and up
+    if (w < kLimbs) sc->t[w] = (uint32_t)lo;
+    if (w + 1 < kLimbs) sc->t[w + 1] = (uint32_t)(lo >> 32);
+    if (w + 2 < kLimbs) sc->t[w + 2] = (uint32_t)hi;
+    int r = 0;
+    for (int j = kLimbs - 1; j >= 0 && r == 0; --j)
+      r = sc->s[j] > sc->t[j] ? 1 : (sc->s[j] < sc->t[j] ? -1 : 0);
+    sc->result = r;
+  }
+  __syncthreads();
+  const int r = sc->result;
+  __syncthreads();
+  return r;
+}
+
+// sign(S - T) from the double-double sum, 2 where it is too close to tell.
+__device__ __forceinline__ int square_sum_cmp_fast(DD ss, double T) {
+  double d, e;
+  two_sum(ss.hi, -T, d, e);
+  const double r = d + (e + ss.lo);
+  const double bound = ss.hi * 0x1p-70;
+  return r > bound ? 1 : (r < -bound ? -1 : 2);
+}
+
+// RN32(S / K), ties to even, for S the exact sum of squares of the row. The
+// decisions are the same in every thread (ss is), so either all threads or
+// none take the exact comparison.
+template <int BS, int NV>
+__device__ __forceinline__ float mean_square_rn32(DD ss, int K, const float (&v)[NV][8], int nvec,
+                                                  SqScratch* sc) {
+  const float c = (float)((ss.hi + ss.lo) / (double)K);    // the answer or a neighbour
+  const uint32_t cb = __float_as_uint(c);
+  // the midpoints below and above c; past the largest finite value the
+  // overflow threshold 2^128 - 2^103 takes the place of a midpoint
+  const double cd = cb == 0x7F800000u ? 0x1p128 : (double)c;
+  const double tl = cb != 0u ? ((double)__uint_as_float(cb - 1u) + cd) * 0.5 : 0.0;
+  const double nd = cb == 0x7F7FFFFFu ? 0x1p128 : (double)__uint_as_float(cb + 1u);
+  const double tu = cb != 0x7F800000u ? (cd + nd) * 0.5 : 0.0;
+  int sl = cb != 0u ? square_sum_cmp_fast(ss, tl * (double)K) : 1;
+  int su = cb != 0x7F800000u ? square_sum_cmp_fast(ss, tu * (double)K) : -1;
+  if (sl == 2 || su == 2) {
+    const int ex = exact_square_sum_cmp<BS, NV>(v, nvec, (sl == 2 ? tl : tu) * (double)K, sc);
+    if (sl == 2) sl = ex;
+    else su = ex;
+  }
+  if (sl < 0 || (sl == 0 && (cb & 1u))) return __uint_as_float(cb - 1u);
+  if (su > 0 || (su == 0 && (cb & 1u))) return __uint_as_float(cb + 1u);
+  return c;
+}
+
+// ---------------------------------------------------------------------------
 // residual add + RMSNorm + quantize: one BS-thread workgroup per row, the row
 // in registers (NV vectors of 8 per thread)
 // ---------------------------------------------------------------------------
@@ -127,6 +247,7 @@ __global__ __launch_bounds__(BS) void rmsnorm_quantize_kernel(
     float* __restrict__ s_tok) {
   __shared__ DD red_dd[BS / kWave];
   __shared__ float red_f[BS / kWave];
+  __shared__ SqScratch sq;
   const int64_t row = blockIdx.x;
   const int tid = threadIdx.x;
   const int nvec = K / 8;
@@ -168,8 +289,8 @@ __global__ __launch_bounds__(BS) void rmsnorm_quantize_kernel(
       }
     }
   }
-  const double ss = block_sum_dd<BS>(acc, red_dd);
-  const float ms = (float)(ss / (double)K);
+  const DD ss = block_sum_dd<BS>(acc, red_dd);
+  const float ms = mean_square_rn32<BS, NV>(ss, K, v, nvec, &sq);
   const float inv = 1.0f / sqrtf(ms + eps);
 
   float amax = 0.0f;

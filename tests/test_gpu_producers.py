@@ -68,6 +68,52 @@ def test_rmsnorm_quantize_edge_rows():
         np.testing.assert_array_equal(host(xq), q_ref)
 
 
+# Pairs of bf16 values whose mean square over K lies exactly halfway between
+# two binary32 values (checked below with exact rationals). For K = 16 and
+# 4096 the tie goes down to the even neighbour, so a tiny extra square (which
+# lifts the mean) changes the rounding and, at eps = 1e-5, the scale; for
+# 14336 = 7 * 2^11 the tie itself goes up.
+MIDPOINT_PAIRS = {16: (2.421875, 0.05615234375), 4096: (129.0, 4.40625),
+                  14336: (175.0, 2.078125)}
+
+
+@pytest.mark.parametrize("K", sorted(MIDPOINT_PAIRS))
+@pytest.mark.parametrize("M", [4, 600])
+@pytest.mark.parametrize("add", [False, True], ids=["norm", "add+norm"])
+def test_rmsnorm_mean_rounded_once_near_midpoints(K, M, add):
+    # A tiny square anywhere in the row (in another thread's vector too) puts
+    # the exact mean just above the midpoint, so its one rounding goes up;
+    # without it the mean is the tie and goes to even. Both take the exact
+    # comparison in the kernel. Random rows fill the rest (600 rows take the
+    # 256/512-thread kernels).
+    from fractions import Fraction
+    a, b = MIDPOINT_PAIRS[K]
+    mean = (Fraction(a) ** 2 + Fraction(b) ** 2) / K
+    assert mean.denominator & (mean.denominator - 1) == 0
+    assert mean.numerator % 2 == 1 and mean.numerator.bit_length() == 25   # a binary32 midpoint
+    tie_goes_down = mean.numerator % 4 == 1
+    rows = O.bf16_to_f32(act(M, K, "rms-mid")).copy()
+    rows[:4] = 0.0
+    rows[:4, :2] = [a, b]
+    rows[0, 2] = 2.0 ** -60
+    rows[2, K - 1] = -(2.0 ** -133)
+    rows[3, 0] = -a
+    rows[3, K // 2 + 3] = 2.0 ** -60
+    h = O.round_to_bf16(rows)
+    assert np.array_equal(O.bf16_to_f32(h[:4]), rows[:4])
+    res = np.zeros_like(h) if add else None
+    g = np.ones(K, F32)
+    for eps in (EPS, 0.0):
+        q_ref, s_ref, _ = O.rmsnorm_quantize(h, res, g, eps)
+        if eps == EPS and tie_goes_down:
+            assert s_ref[0] != s_ref[1]          # the tiny square decides the scale
+        xq, st = W.w8a8_rmsnorm_quantize(dev_bf16(h), dev(g), eps,
+                                         residual=dev_bf16(res) if add else None)
+        torch().cuda.synchronize()
+        np.testing.assert_array_equal(host(st).view(np.uint32), s_ref.view(np.uint32))
+        np.testing.assert_array_equal(host(xq), q_ref)
+
+
 @pytest.mark.parametrize("M,I", [(1, 14336), (16, 14336), (64, 2048), (600, 14336 + 16),
                                  (700, 512)])
 @pytest.mark.parametrize("use_smooth", [False, True], ids=["plain", "smooth"])
