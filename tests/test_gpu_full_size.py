@@ -4,10 +4,12 @@ benchmark times (w8a8_linear on the whole [M, K] x [N, K] problem).
 Both sides start from the same seeded bf16 X and W and each prepares its own
 smoothing factors and int8 weights. The oracle then recomputes a sample: all
 K smoothing factors, a sample of weight rows (their int8 codes and scales),
-a sample of token rows (codes and scales), and the int32 accumulators and
-bf16 outputs on the sampled rows x sampled columns. Rows of both
-quantizations are independent of each other, so a sampled row is checked
-exactly. Properties that hold at any size are checked on the whole output.
+a sample of token rows (codes and scales), and the int32 accumulators (of
+w8a8_gemm_i32 on the whole problem) and bf16 outputs on the sampled rows x
+sampled columns. Rows of both quantizations are independent of each other,
+so a sampled row is checked exactly. Properties that hold at any size are
+checked on the whole output. The second test below compares every element
+of the decode launches and of two prefill launches.
 """
 import numpy as np
 import pytest
@@ -63,8 +65,9 @@ def test_full_size_linear_sampled(wl_name, proj, N, K, M):
     ns = np.unique(np.concatenate([[0, N - 1], r.choice(N, size=min(N, 64), replace=False)]))
     ms_d = torch().from_numpy(ms).cuda()
     ns_d = torch().from_numpy(ns).cuda()
-    acc = W.w8a8_gemm_i32(xq.index_select(0, ms_d).contiguous(),
-                          wq.index_select(0, ns_d).contiguous())
+    # int32 from the whole problem (the kernel route of the timed launch),
+    # then the sampled rows and columns
+    acc = W.w8a8_gemm_i32(xq, wq).index_select(0, ms_d).index_select(1, ns_d)
     torch().cuda.synchronize()
 
     # oracle on the sample
@@ -89,3 +92,78 @@ def test_full_size_linear_sampled(wl_name, proj, N, K, M):
     assert np.all((rowmax == 127) | (host(st) == 0))
     yf = (y_h.astype(np.uint32) << 16).view(np.float32)
     assert np.all(np.isfinite(yf))
+
+
+# ---------------------------------------------------------------------------
+# every element of the full problem
+# ---------------------------------------------------------------------------
+#
+# The launches the benchmark times, compared in full: all 16 Llama-3.1-8B
+# decode (projection, M) pairs and the o and down projections at M = 4096
+# (the prefill kernel at K = 4096 and K = 14336). The int32 accumulators come
+# from w8a8_gemm_i32 on the whole problem (the same kernel route as
+# w8a8_gemm at that shape) and every one is compared with the oracle's
+# integer GEMM; every code, scale and bf16 output of w8a8_linear is compared
+# with the oracle's. The oracle prepares the whole weight (row blocks are
+# independent). Smoothing factors are calibrated on the projection's
+# activations at the largest M of the workload and shared by its smaller M.
+
+EVERY_CASES = ([("llama8b_decode", p, N, K, M) for p, N, K in WL.LLAMA31_8B for M in (1, 4, 16, 64)]
+               + [("llama8b_prefill", p, N, K, 4096) for p, N, K in WL.LLAMA31_8B
+                  if p in ("o", "down")])
+
+_prep = {}
+
+
+def prepared(wl, proj, N, K):
+    """Both sides' smoothing factors and int8 weights for one projection,
+    checked against each other in full once (one entry kept at a time)."""
+    key = (wl.name, proj)
+    if key in _prep:
+        return _prep[key]
+    _prep.clear()
+    out = WL.outlier_channels(K, wl.outlier_frac, wl.name)
+    xcal = WL.activations(max(wl.ms), K, wl.name, proj, 0, outliers=out, mult=wl.outlier_mult)
+    w = WL.weights(N, K, wl.w_std, wl.name, proj, 0)
+    wd = dev_bf16(w)
+    s = W.w8a8_smoothing_factors(W.w8a8_channel_absmax(dev_bf16(xcal)), W.w8a8_channel_absmax(wd))
+    wq, sw = W.w8a8_quantize_weight(wd, s)
+    del wd
+    aw = np.zeros(K, np.float32)
+    for r0 in range(0, N, 4096):
+        aw = np.maximum(aw, O.weight_channel_absmax(w[r0:r0 + 4096]))
+    s_ref = O.smoothing_factors(O.act_channel_absmax(xcal), aw)
+    wq_ref = np.empty((N, K), np.int8)
+    sw_ref = np.empty(N, np.float32)
+    for r0 in range(0, N, 2048):
+        wq_ref[r0:r0 + 2048], sw_ref[r0:r0 + 2048] = O.prepare_weight(w[r0:r0 + 2048], s_ref)
+    torch().cuda.synchronize()
+    np.testing.assert_array_equal(host(s).view(np.uint32), s_ref.view(np.uint32))
+    np.testing.assert_array_equal(host(sw).view(np.uint32), sw_ref.view(np.uint32))
+    np.testing.assert_array_equal(host(wq), wq_ref)
+    _prep[key] = (s, wq, sw, s_ref, wq_ref, sw_ref)
+    return _prep[key]
+
+
+@pytest.mark.parametrize("wl_name,proj,N,K,M", EVERY_CASES,
+                         ids=[f"{c[0]}-{c[1]}-M{c[4]}" for c in EVERY_CASES])
+def test_full_size_every_element(wl_name, proj, N, K, M):
+    wl = WL.WORKLOADS[wl_name]
+    print(f"\n[every element] {wl_name} {proj} M={M} N={N} K={K}", flush=True)
+    s, wq, sw, s_ref, wq_ref, sw_ref = prepared(wl, proj, N, K)
+    out = WL.outlier_channels(K, wl.outlier_frac, wl.name)
+    x = WL.activations(M, K, wl.name, proj, 0, outliers=out, mult=wl.outlier_mult)
+    xd = dev_bf16(x)
+    y = W.w8a8_linear(xd, s, wq, sw)
+    xq, st = W.w8a8_quantize_act(xd, s)
+    acc = W.w8a8_gemm_i32(xq, wq)
+    torch().cuda.synchronize()
+
+    xq_ref, st_ref = O.quantize_act(x, s_ref)
+    np.testing.assert_array_equal(host(st).view(np.uint32), st_ref.view(np.uint32))
+    np.testing.assert_array_equal(host(xq), xq_ref)
+    acc_ref = O.gemm_i32(xq_ref, wq_ref)
+    np.testing.assert_array_equal(host(acc), acc_ref)
+    del acc
+    y64, y_ref = O.dequant_epilogue(acc_ref, st_ref, sw_ref)
+    check_bf16(host(y), y64, y_ref)
