@@ -126,6 +126,41 @@ def _vec(t, name, dtype=None):
     return t.data_ptr()
 
 
+# The C ABI takes bare pointers and cannot see how long a buffer is, so the
+# binding checks every tensor's extent against the sizes it passes before
+# anything reaches the library: a short output would be written past its
+# end, a short input read past it.
+
+def _shape(t, name, rows, cols):
+    if t is None:
+        return
+    if t.dim() != 2 or tuple(t.shape) != (rows, cols):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected ({rows}, {cols})")
+
+
+def _dims(t, name):
+    if t.dim() != 2:
+        raise ValueError(f"{name}: need a 2-D tensor, got shape {tuple(t.shape)}")
+    return tuple(t.shape)
+
+
+def _length(t, name, n):
+    if t is None:
+        return
+    if t.dim() != 1 or t.numel() < n:
+        raise ValueError(f"{name}: {tuple(t.shape)} holds fewer than the {n} elements needed")
+
+
+def _one_device(*tensors):
+    devs = {t.device for t in tensors if t is not None}
+    if len(devs) > 1:
+        raise ValueError(f"tensors on different devices: {sorted(str(d) for d in devs)}")
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
 def _check(status, where):
     if status != 0:
         raise W8A8Error(status, where)
@@ -147,7 +182,11 @@ def w8a8_abi_version() -> int:
 def w8a8_quantize_act(x, smooth=None, xq=None, s_tok=None, stream=None):
     """x bf16 [M, K] -> (xq int8 [M, K], s_tok fp32 [M])."""
     torch = _torch()
-    M, K = x.shape
+    M, K = _dims(x, "x")
+    _length(smooth, "smooth", K)
+    _shape(xq, "xq", M, K)
+    _length(s_tok, "s_tok", M)
+    _one_device(x, smooth, xq, s_tok)
     if xq is None:
         xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
     if s_tok is None:
@@ -162,10 +201,14 @@ def w8a8_quantize_act(x, smooth=None, xq=None, s_tok=None, stream=None):
 def w8a8_gemm(xq, s_tok, wq, s_chan, y=None, stream=None):
     """(xq [M, K], s_tok [M]) x (wq [N, K], s_chan [N]) -> y bf16 [M, N]."""
     torch = _torch()
-    M, K = xq.shape
-    N = wq.shape[0]
-    if wq.shape[1] != K:
-        raise ValueError("xq and wq disagree on K")
+    M, K = _dims(xq, "xq")
+    N, Kw = _dims(wq, "wq")
+    if Kw != K:
+        raise ValueError(f"xq and wq disagree on K ({K} vs {Kw})")
+    _length(s_tok, "s_tok", M)
+    _length(s_chan, "s_chan", N)
+    _shape(y, "y", M, N)
+    _one_device(xq, s_tok, wq, s_chan, y)
     if y is None:
         y = torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
     pq, ldq = _mat(xq, (torch.int8,), "xq")
@@ -179,10 +222,12 @@ def w8a8_gemm(xq, s_tok, wq, s_chan, y=None, stream=None):
 def w8a8_gemm_i32(xq, wq, acc=None, stream=None):
     """Exact int32 accumulators acc [M, N] = xq @ wq.T."""
     torch = _torch()
-    M, K = xq.shape
-    N = wq.shape[0]
-    if wq.shape[1] != K:
-        raise ValueError("xq and wq disagree on K")
+    M, K = _dims(xq, "xq")
+    N, Kw = _dims(wq, "wq")
+    if Kw != K:
+        raise ValueError(f"xq and wq disagree on K ({K} vs {Kw})")
+    _shape(acc, "acc", M, N)
+    _one_device(xq, wq, acc)
     if acc is None:
         acc = torch.empty((M, N), dtype=torch.int32, device=xq.device)
     pq, ldq = _mat(xq, (torch.int8,), "xq")
@@ -200,8 +245,14 @@ def w8a8_linear_workspace_bytes(M: int, K: int) -> int:
 def w8a8_linear(x, smooth, wq, s_chan, y=None, workspace=None, stream=None):
     """x bf16 [M, K] -> y bf16 [M, N] (quantize + GEMM + epilogue)."""
     torch = _torch()
-    M, K = x.shape
-    N = wq.shape[0]
+    M, K = _dims(x, "x")
+    N, Kw = _dims(wq, "wq")
+    if Kw != K:
+        raise ValueError(f"x and wq disagree on K ({K} vs {Kw})")
+    _length(smooth, "smooth", K)
+    _length(s_chan, "s_chan", N)
+    _shape(y, "y", M, N)
+    _one_device(x, smooth, wq, s_chan, y, workspace)
     if y is None:
         y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
     nbytes = w8a8_linear_workspace_bytes(M, K)
@@ -211,8 +262,8 @@ def w8a8_linear(x, smooth, wq, s_chan, y=None, workspace=None, stream=None):
     pw, ldw = _mat(wq, (torch.int8,), "wq")
     py, ldy = _mat(y, _bf16_types(), "y")
     _check(lib().w8a8_linear(px, ldx, _vec(smooth, "smooth"), pw, ldw, _vec(s_chan, "s_chan"),
-                             M, N, K, py, ldy, workspace.data_ptr(),
-                             workspace.numel() * workspace.element_size(), _stream(stream)),
+                             M, N, K, py, ldy, workspace.data_ptr(), _nbytes(workspace),
+                             _stream(stream)),
            "w8a8_linear")
     return y
 
@@ -220,7 +271,9 @@ def w8a8_linear(x, smooth, wq, s_chan, y=None, workspace=None, stream=None):
 def w8a8_channel_absmax(a, absmax=None, stream=None):
     """absmax [K] = max(absmax, max over rows |a|); zero-initialized if not given."""
     torch = _torch()
-    rows, K = a.shape
+    rows, K = _dims(a, "a")
+    _length(absmax, "absmax", K)
+    _one_device(a, absmax)
     if absmax is None:
         absmax = torch.zeros((K,), dtype=torch.float32, device=a.device)
     pa, lda = _mat(a, _bf16_types(), "a")
@@ -232,6 +285,9 @@ def w8a8_channel_absmax(a, absmax=None, stream=None):
 def w8a8_smoothing_factors(act_absmax, w_absmax, smooth=None, stream=None):
     torch = _torch()
     K = act_absmax.shape[0]
+    _length(w_absmax, "w_absmax", K)
+    _length(smooth, "smooth", K)
+    _one_device(act_absmax, w_absmax, smooth)
     if smooth is None:
         smooth = torch.empty((K,), dtype=torch.float32, device=act_absmax.device)
     _check(lib().w8a8_smoothing_factors(_vec(act_absmax, "act_absmax"), _vec(w_absmax, "w_absmax"),
@@ -243,7 +299,11 @@ def w8a8_smoothing_factors(act_absmax, w_absmax, smooth=None, stream=None):
 def w8a8_quantize_weight(w, smooth=None, wq=None, s_chan=None, stream=None):
     """w bf16 [N, K] -> (wq int8 [N, K], s_chan fp32 [N])."""
     torch = _torch()
-    N, K = w.shape
+    N, K = _dims(w, "w")
+    _length(smooth, "smooth", K)
+    _shape(wq, "wq", N, K)
+    _length(s_chan, "s_chan", N)
+    _one_device(w, smooth, wq, s_chan)
     if wq is None:
         wq = torch.empty((N, K), dtype=torch.int8, device=w.device)
     if s_chan is None:
@@ -263,7 +323,12 @@ def w8a8_quantize_weight(w, smooth=None, wq=None, s_chan=None, stream=None):
 def w8a8_quantize_act_static(x, smooth, scale, xq=None, s_tok=None, stream=None):
     """x bf16 [M, K], scale fp32 [1] (device) -> (xq int8 [M, K], s_tok fp32 [M] = scale)."""
     torch = _torch()
-    M, K = x.shape
+    M, K = _dims(x, "x")
+    _length(smooth, "smooth", K)
+    _length(scale, "scale", 1)
+    _shape(xq, "xq", M, K)
+    _length(s_tok, "s_tok", M)
+    _one_device(x, smooth, scale, xq, s_tok)
     if xq is None:
         xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
     if s_tok is None:
@@ -279,8 +344,15 @@ def w8a8_quantize_act_static(x, smooth, scale, xq=None, s_tok=None, stream=None)
 def w8a8_linear_static(x, smooth, scale, wq, s_chan, y=None, workspace=None, stream=None):
     """x bf16 [M, K] -> y bf16 [M, N] with the fixed activation scale scale[0]."""
     torch = _torch()
-    M, K = x.shape
-    N = wq.shape[0]
+    M, K = _dims(x, "x")
+    N, Kw = _dims(wq, "wq")
+    if Kw != K:
+        raise ValueError(f"x and wq disagree on K ({K} vs {Kw})")
+    _length(smooth, "smooth", K)
+    _length(scale, "scale", 1)
+    _length(s_chan, "s_chan", N)
+    _shape(y, "y", M, N)
+    _one_device(x, smooth, scale, wq, s_chan, y, workspace)
     if y is None:
         y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
     nbytes = w8a8_linear_workspace_bytes(M, K)
@@ -291,8 +363,7 @@ def w8a8_linear_static(x, smooth, scale, wq, s_chan, y=None, workspace=None, str
     py, ldy = _mat(y, _bf16_types(), "y")
     _check(lib().w8a8_linear_static(px, ldx, _vec(smooth, "smooth"), _vec(scale, "scale"), pw, ldw,
                                     _vec(s_chan, "s_chan"), M, N, K, py, ldy, workspace.data_ptr(),
-                                    workspace.numel() * workspace.element_size(),
-                                    _stream(stream)),
+                                    _nbytes(workspace), _stream(stream)),
            "w8a8_linear_static")
     return y
 
@@ -301,6 +372,10 @@ def w8a8_calibrate_minmax(act_absmax, smooth=None, amax=None, scale=None, stream
     """Per-channel maxima [K] -> (amax fp32 [1], scale fp32 [1]) on the device."""
     torch = _torch()
     K = act_absmax.shape[0]
+    _length(smooth, "smooth", K)
+    _length(amax, "amax", 1)
+    _length(scale, "scale", 1)
+    _one_device(act_absmax, smooth, amax, scale)
     dev = act_absmax.device
     amax = torch.empty((1,), dtype=torch.float32, device=dev) if amax is None else amax
     scale = torch.empty((1,), dtype=torch.float32, device=dev) if scale is None else scale
@@ -314,7 +389,11 @@ def w8a8_activation_histogram(x, smooth, amax, bins=HIST_BINS, hist=None, stream
     """Adds the |x'| counts of x bf16 [rows, K] to hist (uint32 [bins], kept in
     an int32 tensor; zero-initialized when not given) and returns it."""
     torch = _torch()
-    rows, K = x.shape
+    rows, K = _dims(x, "x")
+    _length(smooth, "smooth", K)
+    _length(amax, "amax", 1)
+    _length(hist, "hist", bins)
+    _one_device(x, smooth, amax, hist)
     if hist is None:
         hist = torch.zeros((bins,), dtype=torch.int32, device=x.device)
     px, ldx = _mat(x, _bf16_types(), "x")
@@ -330,6 +409,10 @@ def w8a8_calibrate_entropy(hist, amax, scale=None, kl=None, want_kl=False, strea
     kl fp64 [bins + 1] or None)."""
     torch = _torch()
     bins = hist.shape[0]
+    _length(amax, "amax", 1)
+    _length(scale, "scale", 1)
+    _length(kl, "kl", bins + 1)
+    _one_device(hist, amax, scale, kl)
     dev = hist.device
     scale = torch.empty((1,), dtype=torch.float32, device=dev) if scale is None else scale
     if kl is None and want_kl:
@@ -350,7 +433,12 @@ def w8a8_rmsnorm_quantize(h, gamma, eps=1e-5, residual=None, xq=None, s_tok=None
     """(residual add into h,) RMSNorm with the folded weight, per-token codes.
     h bf16 [M, K] (updated in place when residual is given) -> (xq, s_tok)."""
     torch = _torch()
-    M, K = h.shape
+    M, K = _dims(h, "h")
+    _length(gamma, "gamma", K)
+    _shape(residual, "residual", M, K)
+    _shape(xq, "xq", M, K)
+    _length(s_tok, "s_tok", M)
+    _one_device(h, gamma, residual, xq, s_tok)
     if xq is None:
         xq = torch.empty((M, K), dtype=torch.int8, device=h.device)
     if s_tok is None:
@@ -367,8 +455,14 @@ def w8a8_rmsnorm_quantize(h, gamma, eps=1e-5, residual=None, xq=None, s_tok=None
 def w8a8_silu_mul_quantize(gu, smooth=None, xq=None, s_tok=None, stream=None):
     """gu bf16 [M, 2I] (gate | up) -> (xq int8 [M, I], s_tok fp32 [M])."""
     torch = _torch()
-    M, two_i = gu.shape
+    M, two_i = _dims(gu, "gu")
+    if two_i % 2:
+        raise ValueError(f"gu: width {two_i} is not gate | up of equal halves")
     inter = two_i // 2
+    _length(smooth, "smooth", inter)
+    _shape(xq, "xq", M, inter)
+    _length(s_tok, "s_tok", M)
+    _one_device(gu, smooth, xq, s_tok)
     if xq is None:
         xq = torch.empty((M, inter), dtype=torch.int8, device=gu.device)
     if s_tok is None:
@@ -384,6 +478,9 @@ def w8a8_silu_mul_quantize(gu, smooth=None, xq=None, s_tok=None, stream=None):
 def w8a8_fold_gamma(gamma, smooth=None, g=None, stream=None):
     torch = _torch()
     K = gamma.shape[0]
+    _length(smooth, "smooth", K)
+    _length(g, "g", K)
+    _one_device(gamma, smooth, g)
     if g is None:
         g = torch.empty((K,), dtype=torch.float32, device=gamma.device)
     _check(lib().w8a8_fold_gamma(_vec(gamma, "gamma"), _vec(smooth, "smooth"), K, _vec(g, "g"),
@@ -393,7 +490,9 @@ def w8a8_fold_gamma(gamma, smooth=None, g=None, stream=None):
 
 def w8a8_residual_add(h, r, stream=None):
     """h = bf16(h + r) in place."""
-    M, K = h.shape
+    M, K = _dims(h, "h")
+    _shape(r, "r", M, K)
+    _one_device(h, r)
     ph, ldh = _mat(h, _bf16_types(), "h")
     pr, ldr = _mat(r, _bf16_types(), "r")
     _check(lib().w8a8_residual_add(ph, ldh, pr, ldr, M, K, _stream(stream)), "w8a8_residual_add")
@@ -414,7 +513,10 @@ def _dense_f64(t, name):
 def w8a8_gptq_hessian(x, smooth=None, H=None, stream=None):
     """H [K, K] float64 += 2 x'^T x' (zero-initialized when not given)."""
     torch = _torch()
-    n, K = x.shape
+    n, K = _dims(x, "x")
+    _length(smooth, "smooth", K)
+    _shape(H, "H", K, K)
+    _one_device(x, smooth, H)
     if H is None:
         H = torch.zeros((K, K), dtype=torch.float64, device=x.device)
     px, ldx = _mat(x, _bf16_types(), "x")
@@ -431,13 +533,16 @@ def w8a8_gptq_factor(H, damp=0.01, U=None, workspace=None, stream=None):
     """U [K, K] float64, upper, U^T U = (H + lambda I)^-1."""
     torch = _torch()
     K = H.shape[0]
+    _shape(H, "H", K, K)
+    _shape(U, "U", K, K)
+    _one_device(H, U, workspace)
     if U is None:
         U = torch.empty((K, K), dtype=torch.float64, device=H.device)
     nbytes = w8a8_gptq_factor_workspace_bytes(K)
     if workspace is None:
         workspace = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=H.device)
     _check(lib().w8a8_gptq_factor(_dense_f64(H, "H"), K, float(damp), _dense_f64(U, "U"),
-                                  workspace.data_ptr(), workspace.numel(), _stream(stream)),
+                                  workspace.data_ptr(), _nbytes(workspace), _stream(stream)),
            "w8a8_gptq_factor")
     return U
 
@@ -449,7 +554,12 @@ def w8a8_gptq_quantize_workspace_bytes(N: int, K: int) -> int:
 def w8a8_gptq_quantize(w, smooth, U, wq=None, s_chan=None, workspace=None, stream=None):
     """w bf16 [N, K] -> (wq int8 [N, K], s_chan fp32 [N]) with GPTQ error feedback."""
     torch = _torch()
-    N, K = w.shape
+    N, K = _dims(w, "w")
+    _length(smooth, "smooth", K)
+    _shape(U, "U", K, K)
+    _shape(wq, "wq", N, K)
+    _length(s_chan, "s_chan", N)
+    _one_device(w, smooth, U, wq, s_chan, workspace)
     if wq is None:
         wq = torch.empty((N, K), dtype=torch.int8, device=w.device)
     if s_chan is None:
@@ -461,5 +571,5 @@ def w8a8_gptq_quantize(w, smooth, U, wq=None, s_chan=None, workspace=None, strea
     pq, ldq = _mat(wq, (torch.int8,), "wq")
     _check(lib().w8a8_gptq_quantize(pw, ldw, _vec(smooth, "smooth"), _dense_f64(U, "U"), N, K,
                                     pq, ldq, _vec(s_chan, "s_chan"), workspace.data_ptr(),
-                                    workspace.numel(), _stream(stream)), "w8a8_gptq_quantize")
+                                    _nbytes(workspace), _stream(stream)), "w8a8_gptq_quantize")
     return wq, s_chan

@@ -4,6 +4,7 @@ HIP call. Every call below with fake pointers either fails validation or is
 an empty (M == 0 / N == 0) no-op, so nothing is ever launched, even on a
 machine with a GPU."""
 import ctypes
+import re
 import subprocess
 
 import pytest
@@ -202,3 +203,56 @@ def test_python_binding_raises_typed_error(lib):
     torch = pytest.importorskip("torch")
     with pytest.raises((TypeError, ValueError)):
         W.w8a8_quantize_act(torch.zeros((4, 16), dtype=torch.float32))
+
+
+def test_binding_checks_every_extent(lib):
+    # The ABI sees bare pointers, so the binding must refuse buffers that do
+    # not match the sizes it passes. These are host tensors: the extent checks
+    # come before the device check, so each call stops at the size it names.
+    torch = pytest.importorskip("torch")
+    bf, i8, f32 = torch.bfloat16, torch.int8, torch.float32
+    e = lambda *s, dt=f32: torch.empty(s, dtype=dt)      # noqa: E731
+    M, N, K = 4, 32, 64
+    x, wq, xq = e(M, K, dt=bf), e(N, K, dt=i8), e(M, K, dt=i8)
+    cases = [
+        (lambda: W.w8a8_quantize_act(x, smooth=e(K - 1)), "smooth"),
+        (lambda: W.w8a8_quantize_act(x, xq=e(M - 1, K, dt=i8)), "xq"),
+        (lambda: W.w8a8_quantize_act(x, s_tok=e(M - 1)), "s_tok"),
+        (lambda: W.w8a8_gemm(xq, e(M - 1), wq, e(N)), "s_tok"),
+        (lambda: W.w8a8_gemm(xq, e(M), wq, e(N - 1)), "s_chan"),
+        (lambda: W.w8a8_gemm(xq, e(M), e(N, K + 16, dt=i8), e(N)), "disagree on K"),
+        (lambda: W.w8a8_gemm(xq, e(M), wq, e(N), y=e(M - 1, N, dt=bf)), "y"),
+        (lambda: W.w8a8_gemm_i32(xq, wq, acc=e(M, N - 1, dt=torch.int32)), "acc"),
+        (lambda: W.w8a8_linear(x, e(K - 1), wq, e(N)), "smooth"),
+        (lambda: W.w8a8_linear(x, None, wq, e(N - 1)), "s_chan"),
+        (lambda: W.w8a8_linear(x, None, e(N, 2 * K, dt=i8), e(N)), "disagree on K"),
+        (lambda: W.w8a8_linear(x, None, wq, e(N), y=e(M - 1, N, dt=bf)), "y"),
+        (lambda: W.w8a8_channel_absmax(x, absmax=e(K - 1)), "absmax"),
+        (lambda: W.w8a8_smoothing_factors(e(K), e(K - 1)), "w_absmax"),
+        (lambda: W.w8a8_quantize_weight(e(N, K, dt=bf), e(K - 1)), "smooth"),
+        (lambda: W.w8a8_quantize_weight(e(N, K, dt=bf), wq=e(N, K - 16, dt=i8)), "wq"),
+        (lambda: W.w8a8_quantize_weight(e(N, K, dt=bf), s_chan=e(N - 1)), "s_chan"),
+        (lambda: W.w8a8_quantize_act_static(x, None, e(0)), "scale"),
+        (lambda: W.w8a8_linear_static(x, None, e(1), wq, e(N - 1)), "s_chan"),
+        (lambda: W.w8a8_calibrate_minmax(e(K), e(K - 1)), "smooth"),
+        (lambda: W.w8a8_activation_histogram(x, None, e(1), hist=e(2047, dt=torch.int32)), "hist"),
+        (lambda: W.w8a8_calibrate_entropy(e(2048, dt=torch.int32), e(1),
+                                          kl=e(2048, dt=torch.float64)), "kl"),
+        (lambda: W.w8a8_rmsnorm_quantize(x, e(K - 1)), "gamma"),
+        (lambda: W.w8a8_rmsnorm_quantize(x, e(K), residual=e(M, K - 16, dt=bf)), "residual"),
+        (lambda: W.w8a8_silu_mul_quantize(e(M, 2 * K + 1, dt=bf)), "gate | up"),
+        (lambda: W.w8a8_silu_mul_quantize(e(M, 2 * K, dt=bf), e(K - 1)), "smooth"),
+        (lambda: W.w8a8_silu_mul_quantize(e(M, 2 * K, dt=bf), xq=e(M, 2 * K, dt=i8)), "xq"),
+        (lambda: W.w8a8_fold_gamma(e(K), e(K - 1)), "smooth"),
+        (lambda: W.w8a8_residual_add(x, e(M, K - 16, dt=bf)), "r"),
+        (lambda: W.w8a8_gptq_hessian(x, H=e(K, K - 1, dt=torch.float64)), "H"),
+        (lambda: W.w8a8_gptq_factor(e(K, K - 1, dt=torch.float64)), "H"),
+        (lambda: W.w8a8_gptq_quantize(e(N, K, dt=bf), None, e(K - 1, K, dt=torch.float64)), "U"),
+    ]
+    for call, what in cases:
+        pattern = f"^{what}: " if what.isidentifier() else re.escape(what)
+        with pytest.raises(ValueError, match=pattern):
+            call()
+    # with every extent right, a host tensor stops at the device check
+    with pytest.raises(ValueError, match="device tensor"):
+        W.w8a8_gemm(xq, e(M), wq, e(N), y=e(M, N, dt=bf))
