@@ -21,7 +21,10 @@
  *     before the GPU work completes. The caller owns all memory; inputs and
  *     outputs must stay valid until the stream reaches the call. The library
  *     never allocates device memory; the only state it keeps between calls
- *     is each device's compute-unit count, read once for tile choices.
+ *     is each device's compute-unit count, read once for tile choices, and
+ *     each device's address of the fixed workspace array that
+ *     w8a8_linear_noalloc uses (8 MiB per device, held until the process
+ *     ends).
  *   - Arguments are validated on the host before any HIP call. A failed
  *     check returns an error status and enqueues nothing. Device faults
  *     surface at the caller's next synchronization, as for any HIP kernel.
@@ -144,6 +147,30 @@ w8a8_status_t w8a8_linear(const uint16_t* x, int64_t ldx, const float* smooth,
                           uint16_t* y, int64_t ldy,
                           void* workspace, size_t workspace_bytes,
                           hipStream_t stream);
+
+/*
+ * w8a8_linear for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation and results, with the workspace taken from one fixed
+ * device array inside the library instead of a caller buffer. The call
+ * itself allocates nothing.
+ *   Same arguments as w8a8_linear without the workspace.
+ *   Limit: w8a8_linear_workspace_bytes(M, K) <= W8A8_NOALLOC_MAX_BYTES
+ *   (8 MiB: M * K up to about 8.3 million, e.g. 64 tokens at K = 131072 or
+ *   2048 tokens at K = 4096); larger sizes return W8A8_ERROR_WORKSPACE and
+ *   enqueue nothing. Each device holds its own 8 MiB array until the
+ *   process ends; its address is looked up on the first call on a device
+ *   (W8A8_ERROR_HIP if that fails).
+ *   Every call on a device uses that device's one array: calls that may
+ *   overlap on one device (different streams, or another thread's calls)
+ *   race and must be serialized by the caller. Nothing in the array needs
+ *   to start at zero; each call overwrites what it reads.
+ */
+#define W8A8_NOALLOC_MAX_BYTES (8u << 20)
+w8a8_status_t w8a8_linear_noalloc(const uint16_t* x, int64_t ldx, const float* smooth,
+                                  const int8_t* wq, int64_t ldw, const float* s_chan,
+                                  int64_t M, int64_t N, int64_t K,
+                                  uint16_t* y, int64_t ldy, hipStream_t stream);
 
 /* ----------------------------------------------------------------------- *
  * Offline preparation (calibration and weight quantization). These run

@@ -7,6 +7,7 @@ function for function.
 """
 from .binding import (  # noqa: F401
     HIST_BINS,
+    NOALLOC_MAX_BYTES,
     QUANT_LEVELS,
     W8A8Error,
     header_functions,
@@ -25,6 +26,7 @@ from .binding import (  # noqa: F401
     w8a8_gptq_quantize,
     w8a8_gptq_quantize_workspace_bytes,
     w8a8_linear,
+    w8a8_linear_noalloc,
     w8a8_linear_static,
     w8a8_linear_workspace_bytes,
     w8a8_quantize_act,

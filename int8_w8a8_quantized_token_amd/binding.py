@@ -37,6 +37,7 @@ _SIGNATURES = {
     "w8a8_gemm_i32": (_i, [_p, _i64, _p, _i64, _i64, _i64, _i64, _p, _i64, _p]),
     "w8a8_linear_workspace_bytes": (_sz, [_i64, _i64]),
     "w8a8_linear": (_i, [_p, _i64, _p, _p, _i64, _p, _i64, _i64, _i64, _p, _i64, _p, _sz, _p]),
+    "w8a8_linear_noalloc": (_i, [_p, _i64, _p, _p, _i64, _p, _i64, _i64, _i64, _p, _i64, _p]),
     "w8a8_channel_absmax": (_i, [_p, _i64, _i64, _i64, _p, _p]),
     "w8a8_smoothing_factors": (_i, [_p, _p, _i64, _p, _p]),
     "w8a8_quantize_weight": (_i, [_p, _i64, _p, _i64, _i64, _p, _i64, _p, _p]),
@@ -265,6 +266,33 @@ def w8a8_linear(x, smooth, wq, s_chan, y=None, workspace=None, stream=None):
                              M, N, K, py, ldy, workspace.data_ptr(), _nbytes(workspace),
                              _stream(stream)),
            "w8a8_linear")
+    return y
+
+
+NOALLOC_MAX_BYTES = 8 << 20   # W8A8_NOALLOC_MAX_BYTES
+
+
+def w8a8_linear_noalloc(x, smooth, wq, s_chan, y=None, stream=None):
+    """w8a8_linear with the library's fixed workspace (no workspace argument;
+    the library call allocates nothing). Pass y to allocate nothing here
+    either."""
+    torch = _torch()
+    M, K = _dims(x, "x")
+    N, Kw = _dims(wq, "wq")
+    if Kw != K:
+        raise ValueError(f"x and wq disagree on K ({K} vs {Kw})")
+    _length(smooth, "smooth", K)
+    _length(s_chan, "s_chan", N)
+    _shape(y, "y", M, N)
+    _one_device(x, smooth, wq, s_chan, y)
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    px, ldx = _mat(x, _bf16_types(), "x")
+    pw, ldw = _mat(wq, (torch.int8,), "wq")
+    py, ldy = _mat(y, _bf16_types(), "y")
+    _check(lib().w8a8_linear_noalloc(px, ldx, _vec(smooth, "smooth"), pw, ldw,
+                                     _vec(s_chan, "s_chan"), M, N, K, py, ldy, _stream(stream)),
+           "w8a8_linear_noalloc")
     return y
 
 

@@ -4,6 +4,8 @@
 #include <limits.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/w8a8.h"
 #include "launchers.h"
 
@@ -152,6 +154,63 @@ w8a8_status_t w8a8_linear(const uint16_t* x, int64_t ldx, const float* smooth, c
                                                xq, K, s_tok, stream)));
   return from_hip(w8a8::launch_gemm(xq, K, s_tok, wq, ldw, s_chan, M, N, K, y, ldy, nullptr, 0,
                                     stream));
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// w8a8_linear without a caller workspace
+// ---------------------------------------------------------------------------
+//
+// For callers that cannot allocate device memory: the workspace of
+// w8a8_linear (codes and token scales) lives in one fixed device array.
+// Each device holds its own copy of the array, at its own address, from the
+// library's load until the process ends. In host code the array's name is
+// only a stand-in, so its device address is taken once per device with
+// hipGetSymbolAddress and kept; kernels receive that address.
+
+namespace {
+
+static __device__ __align__(256) unsigned char scratch[W8A8_NOALLOC_MAX_BYTES];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices];
+
+// The current device's copy of the array (nullptr if it cannot be found).
+void* scratch_on_current_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+w8a8_status_t w8a8_linear_noalloc(const uint16_t* x, int64_t ldx, const float* smooth,
+                                  const int8_t* wq, int64_t ldw, const float* s_chan, int64_t M,
+                                  int64_t N, int64_t K, uint16_t* y, int64_t ldy,
+                                  hipStream_t stream) {
+  W8A8_TRY(check_dims(M, K, N));
+  if (M == 0 || N == 0) return W8A8_SUCCESS;
+  W8A8_TRY(check_matrix(x, ldx, M, K, 2));
+  W8A8_TRY(check_matrix(wq, ldw, N, K, 1));
+  W8A8_TRY(check_vector(s_chan));
+  if (smooth) W8A8_TRY(check_vector(smooth));
+  W8A8_TRY(check_out_matrix(y, ldy, M, N, 2));
+  if (w8a8_linear_workspace_bytes(M, K) > (size_t)W8A8_NOALLOC_MAX_BYTES)
+    return W8A8_ERROR_WORKSPACE;
+  void* ws = scratch_on_current_device();
+  if (ws == nullptr) return W8A8_ERROR_HIP;
+  return w8a8_linear(x, ldx, smooth, wq, ldw, s_chan, M, N, K, y, ldy, ws,
+                     (size_t)W8A8_NOALLOC_MAX_BYTES, stream);
 }
 
 w8a8_status_t w8a8_quantize_act_static(const uint16_t* x, int64_t ldx, const float* smooth,

@@ -24,7 +24,7 @@ def lib():
 
 def test_exports_every_header_function(lib):
     names = W.header_functions()
-    assert len(names) == 24
+    assert len(names) == 25
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
@@ -106,6 +106,21 @@ def test_linear_validation(lib):
     assert lin(lib, x=None) == INVALID
     assert lin(lib, M=0, ws=None, x=None) == OK
     assert lin(lib, K=4104) == UNSUPPORTED
+
+
+def test_linear_noalloc_validation(lib):
+    f = lib.w8a8_linear_noalloc
+    def call(M=16, N=4096, K=4096, x=A, y=A):
+        return f(x, K, None, A, K, A, M, N, K, y, N, None)
+    assert call(M=2048) == WORKSPACE             # workspace past the fixed 8 MiB
+    assert call(M=1 << 20, K=16) == WORKSPACE
+    assert call(x=None) == INVALID
+    assert call(y=None) == INVALID
+    assert call(K=4104) == UNSUPPORTED
+    assert call(x=MIS) == MISALIGNED
+    assert call(M=0, x=None, y=None) == OK        # empty call, nothing launched
+    assert W.w8a8_linear_workspace_bytes(2046, 4096) <= B.NOALLOC_MAX_BYTES
+    assert W.w8a8_linear_workspace_bytes(2047, 4096) > B.NOALLOC_MAX_BYTES
 
 
 def test_prep_validation(lib):
