@@ -23,11 +23,13 @@ duration is the graph time over the number of launches.
 Also reported: the decode step split by token count (decode_by_m, whole
 linear and GEMM alone against the HBM peak); the same decode step with one
 calibrated activation scale per projection (static_decode); a 32-layer
-block chain at 3000 tokens with the fused norm and SiLU producers (chain);
-the Llama-3-70B projections at
-32 and 2048 tokens (llama70b); the cost of a kernel boundary in a graph
-(dispatch_floor_us); the shader and memory clocks before and after; and
-the CPU oracle on a bounded sample (cpu_baseline). --detail adds per-shape
+block chain at 3000 tokens with the fused norm and SiLU producers (chain),
+with its drift from an unquantized fp32 forward after 1, 8 and 32 layers;
+the Llama-3-70B projections at 32 and 2048 tokens (llama70b); the cost of a
+kernel boundary in a graph (dispatch_floor_us); the shader and memory clocks
+before and after; and the CPU oracle on a bounded sample beside each line
+(cpu_baseline at the top level for decode, and inside prefill, chain and
+llama70b). --detail adds per-shape
 times of the linear, the GEMM alone and the quantizer alone; --counters
 only launches every GEMM once for hardware-counter passes.
 """
@@ -128,12 +130,14 @@ class Setup:
         dev = "cuda"
         self.s, self.sw, self.wq, self.S_static = {}, {}, {}, {}
         self.x, self.y, self.ws, self.xq, self.st = {}, {}, {}, {}, {}
+        self.w_host = {}        # the unquantized bf16 weights (drift reference of the chain)
         t0 = time.time()
         for proj, N, K in self.shapes:
             outl = WL.outlier_channels(K, wl.outlier_frac, wl.name)
             xcal = WL.activations(PREFILL_M, K, wl.name, proj, 0, outliers=outl,
                                   mult=wl.outlier_mult)
             w = WL.weights(N, K, wl.w_std, wl.name, proj, 0)
+            self.w_host[proj] = w
             xcal_d = self.bf16(xcal)
             w_d = self.bf16(w)
             # offline prep on the GPU: calibrate, smooth, quantize per channel
@@ -384,12 +388,68 @@ def run_chain(torch, W, WL, S, args):
     tops = ops / (t_full * 1e-3) / 1e12
     log(f"[bench] chain: 32 layers x {M} tokens {t_full:.3f} ms ({tops:.0f} TOPS); "
         f"producers alone {t_prod:.3f} ms ({pbytes / (t_prod * 1e-3) / 1e9:.0f} GB/s)")
-    return {"value": round(tops, 1), "unit": "TOPS", "ms_per_forward": round(t_full, 4),
-            "producers_ms": round(t_prod, 4),
-            "producers_GBps": round(pbytes / (t_prod * 1e-3) / 1e9, 1),
-            "config": {"workload": "llama8b_chain: 32 layers x (fused norm/SiLU producers + "
-                                   "4 W8A8 GEMMs), 3000 tokens, q slice for attention",
-                       "tokens": M}}
+    out = {"value": round(tops, 1), "unit": "TOPS", "ms_per_forward": round(t_full, 4),
+           "producers_ms": round(t_prod, 4),
+           "producers_GBps": round(pbytes / (t_prod * 1e-3) / 1e9, 1),
+           "config": {"workload": "llama8b_chain: 32 layers x (fused norm/SiLU producers + "
+                                  "4 W8A8 GEMMs), 3000 tokens, q slice for attention",
+                      "tokens": M}}
+
+    # drift of the W8A8 chain from the unquantized model: the residual stream
+    # of sampled token rows after 1, 8 and 32 layers against an fp32 forward
+    # of the same block structure with the bf16 weights unquantized (RMSNorm
+    # with gamma, no smoothing: it cancels in exact arithmetic)
+    import numpy as np
+    t0 = time.time()
+    rows = np.sort(WL.rng("chain-drift").choice(M, size=8, replace=False))
+    rows_d = torch.from_numpy(rows).to(dev)
+    snaps = {}
+    h.copy_(x0)
+    pending = None
+    for layer in range(LAYERS):
+        W.w8a8_rmsnorm_quantize(h, g_attn, 1e-5, residual=pending, xq=q_view(hid), s_tok=st)
+        W.w8a8_gemm(q_view(hid), st, S.wq["qkv"][layer], S.sw["qkv"], y=y["qkv"])
+        W.w8a8_quantize_act(y["qkv"][:, :hid], S.s["o"], xq=q_view(hid), s_tok=st)
+        W.w8a8_gemm(q_view(hid), st, S.wq["o"][layer], S.sw["o"], y=y["o"])
+        W.w8a8_rmsnorm_quantize(h, g_mlp, 1e-5, residual=y["o"], xq=q_view(hid), s_tok=st)
+        W.w8a8_gemm(q_view(hid), st, S.wq["gate_up"][layer], S.sw["gate_up"], y=y["gate_up"])
+        W.w8a8_silu_mul_quantize(y["gate_up"], S.s["down"], xq=xq, s_tok=st)
+        W.w8a8_gemm(xq, st, S.wq["down"][layer], S.sw["down"], y=y["down"])
+        pending = y["down"]
+        if layer + 1 in (1, 8, LAYERS):
+            hs = h.index_select(0, rows_d).contiguous()
+            W.w8a8_residual_add(hs, pending.index_select(0, rows_d).contiguous())
+            snaps[layer + 1] = hs.view(torch.int16).cpu().numpy().view(np.uint16)
+    torch.cuda.synchronize()
+
+    def f32(u16):
+        return (np.asarray(u16, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+    wf = {p: f32(S.w_host[p]) for p in shp}
+    gam = np.ones(hid, np.float32)
+    gam[outl] = 20.0
+    x_host = WL.activations(M, hid, "llama8b_chain", "x", outliers=outl)
+    href = f32(x_host[rows]).astype(np.float32)
+
+    def rmsnorm(a):
+        return a / np.sqrt(np.mean(a * a, axis=1, keepdims=True) + np.float32(1e-5)) * gam
+
+    drift = {}
+    for layer in range(LAYERS):
+        qkv = rmsnorm(href) @ wf["qkv"].T
+        href = href + qkv[:, :hid] @ wf["o"].T
+        gu = rmsnorm(href) @ wf["gate_up"].T
+        g, u = gu[:, :inter], gu[:, inter:]
+        href = href + ((g / (np.float32(1) + np.exp(-g))) * u) @ wf["down"].T
+        if layer + 1 in snaps:
+            d = f32(snaps[layer + 1]).astype(np.float64) - href.astype(np.float64)
+            drift[str(layer + 1)] = round(float(np.linalg.norm(d) / np.linalg.norm(href)), 5)
+    out["drift_vs_fp32"] = {
+        "rel_err_after_layers": drift, "rows": len(rows),
+        "reference": "fp32 forward of the unquantized block stack (bf16 weights, RMSNorm with "
+                     "gamma), sampled token rows; error = ||h_w8a8 - h_fp32|| / ||h_fp32||"}
+    log(f"[bench] chain drift vs fp32 ({time.time() - t0:.1f}s): {drift}")
+    return out
 
 
 def run_70b(torch, W, WL, args):
@@ -454,15 +514,50 @@ def _bf16_dev(torch, u16):
     return torch.from_numpy(np.ascontiguousarray(u16).view(np.int16)).cuda().view(torch.bfloat16)
 
 
-def cpu_baseline(W, WL, sample_ms, min_seconds=10.0):
-    """The oracle, timed on this host on one layer of the decode workload."""
-    import numpy as np
-    from oracle import w8a8_oracle as O
+def _cpu_host():
+    """BLAS threads the oracle's matmul uses, the CPU model and the CPUs in
+    this process's affinity mask."""
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
         threads = 1
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")),
+                         model)
+    except OSError:
+        pass
+    return {"cores": int(threads), "kind": "oracle", "cpu_model": model,
+            "cpus_in_affinity": len(os.sched_getaffinity(0))}
+
+
+def _time_passes(one_pass, min_seconds):
+    """Whole passes of one_pass() (which returns (seconds, work)) until the
+    oracle time reaches min_seconds. Returns (seconds, work, passes)."""
+    t = work = 0.0
+    passes = 0
+    while t < min_seconds:
+        dt, dw = one_pass()
+        t += dt
+        work += dw
+        passes += 1
+    return t, work, passes
+
+
+def cpu_baselines(W, WL, sample_ms, min_seconds=10.0):
+    """The oracle, timed on this host beside every GPU line, each on a bounded
+    sample of the line's workload (weight preparation untimed):
+      decode:  whole passes over one layer's four projections at M in sample_ms;
+      prefill: the first 512 of the 4096 token rows of each projection (rows
+               are independent, so the rate stands for the whole linear);
+      chain:   4 token rows through 2 layers of the block chain;
+      llama70b: 1024 output channels of each 70B projection (weights drawn at
+               that size), at 32 tokens and at 256 of the 2048 token rows."""
+    import numpy as np
+    from oracle import w8a8_oracle as O
+    host = _cpu_host()
     wl = WL.WORKLOADS["llama8b_decode"]
     prepared = []
     for proj, N, K in wl.shapes:
@@ -478,29 +573,105 @@ def cpu_baseline(W, WL, sample_ms, min_seconds=10.0):
         sw = np.concatenate([p[1] for p in parts])
         xs = {M: WL.activations(M, K, wl.name, proj, 0, outliers=outl, mult=wl.outlier_mult)
               for M in sample_ms}
+        xs["prefill"] = np.ascontiguousarray(xcal[:512])
         prepared.append((proj, N, K, s, wq, sw, xs))
-    nbytes, t, passes = 0, 0.0, 0
-    while t < min_seconds:                  # whole passes until the budget is spent
+
+    def timed_linear(x, s, wq, sw):
+        t0 = time.perf_counter()
+        O.linear(x, s, wq, sw)
+        return time.perf_counter() - t0
+
+    # decode: GB/s of algorithmic bytes
+    def decode_pass():
+        t = b = 0.0
         for M in sample_ms:
             for proj, N, K, s, wq, sw, xs in prepared:
-                t0 = time.perf_counter()
-                O.linear(xs[M], s, wq, sw)
-                t += time.perf_counter() - t0
-                nbytes += lin_bytes(M, N, K)
+                t += timed_linear(xs[M], s, wq, sw)
+                b += lin_bytes(M, N, K)
+        return t, b
+    t, nbytes, passes = _time_passes(decode_pass, min_seconds)
+    decode = {"value": round(nbytes / t / 1e9, 3), "unit": "GB/s", **host,
+              "sample": f"{passes} pass(es) over one layer (qkv, o, gate_up, down) of the decode "
+                        f"workload at M in {list(sample_ms)}: {passes * len(sample_ms) * 4} oracle "
+                        f"linears, {nbytes / 1e9:.2f} GB algorithmic, {t:.1f} s of oracle time; "
+                        f"weight prep untimed"}
+
+    # prefill: TOPS on a row sample of the M = 4096 activations
+    def prefill_pass():
+        t = ops = 0.0
+        for proj, N, K, s, wq, sw, xs in prepared:
+            x = xs["prefill"]
+            t += timed_linear(x, s, wq, sw)
+            ops += 2.0 * x.shape[0] * N * K
+        return t, ops
+    t, ops, passes = _time_passes(prefill_pass, 0.8 * min_seconds)
+    prefill = {"value": round(ops / t / 1e12, 4), "unit": "TOPS", **host,
+               "sample": f"{passes} pass(es) of the oracle linear on the first 512 of the 4096 "
+                         f"token rows of each projection (qkv, o, gate_up, down; whole weights): "
+                         f"{ops / 1e12:.2f} T int8 ops in {t:.1f} s; weight prep untimed"}
+
+    # chain: TOPS of the oracle's block chain on a few token rows
+    byp = {p[0]: p for p in prepared}
+    hid = 4096
+    outl = WL.outlier_channels(hid, 0.01, "llama8b_chain")
+    gamma = np.ones(hid, np.float32)
+    gamma[outl] = 20.0
+    layer = {"g_attn": O.fold_gamma(gamma, byp["qkv"][3]),
+             "g_mlp": O.fold_gamma(gamma, byp["gate_up"][3]),
+             "s_o": byp["o"][3], "s_down": byp["down"][3],
+             **{p: (byp[p][4], byp[p][5]) for p in byp}}
+    rows = 4
+    x_chain = np.ascontiguousarray(
+        WL.activations(CHAIN_M, hid, "llama8b_chain", "x", outliers=outl)[:rows])
+    chain_ops = 2.0 * rows * sum(N * K for _, N, K in wl.shapes) * 2
+
+    def chain_pass():
+        t0 = time.perf_counter()
+        O.chain_forward(x_chain, [layer, layer])
+        return time.perf_counter() - t0, chain_ops
+    t, ops, passes = _time_passes(chain_pass, 0.6 * min_seconds)
+    chain = {"value": round(ops / t / 1e12, 5), "unit": "TOPS", **host,
+             "sample": f"{passes} pass(es) of the oracle block chain on {rows} token rows "
+                       f"through 2 layers (8 linears, norms, SiLU producer): {ops / 1e9:.1f} G "
+                       f"int8 ops in {t:.1f} s; weight prep untimed"}
+
+    # Llama-3-70B: 1024 output channels per projection
+    w70 = WL.WORKLOADS["llama70b"]
+    m_dec, m_pf = w70.ms
+    nsamp, psamp = 1024, 256
+    prep70 = []
+    for proj, _, K in w70.shapes:
+        outl = WL.outlier_channels(K, w70.outlier_frac, w70.name)
+        x = WL.activations(m_pf, K, w70.name, proj, 0, outliers=outl, mult=w70.outlier_mult)
+        w = WL.weights(nsamp, K, w70.w_std, w70.name, proj, "cpu-sample")
+        s = O.smoothing_factors(O.act_channel_absmax(x), O.weight_channel_absmax(w))
+        wq, sw = O.prepare_weight(w, s)
+        prep70.append((K, s, wq, sw, np.ascontiguousarray(x[:m_dec]),
+                       np.ascontiguousarray(x[:psamp])))
+
+    def b70_pass():
+        td = tp = b = ops = 0.0
+        for K, s, wq, sw, xd, xp in prep70:
+            td += timed_linear(xd, s, wq, sw)
+            b += lin_bytes(m_dec, nsamp, K)
+            tp += timed_linear(xp, s, wq, sw)
+            ops += 2.0 * psamp * nsamp * K
+        return td + tp, (td, b, tp, ops)
+    acc = [0.0, 0.0, 0.0, 0.0]
+    spent = 0.0
+    passes = 0
+    while spent < 0.6 * min_seconds:
+        dt, parts = b70_pass()
+        spent += dt
+        acc = [a + p for a, p in zip(acc, parts)]
         passes += 1
-    model = "unknown"
-    try:
-        with open("/proc/cpuinfo") as f:
-            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")),
-                         model)
-    except OSError:
-        pass
-    return {"value": round(nbytes / t / 1e9, 3), "unit": "GB/s", "cores": int(threads),
-            "kind": "oracle", "cpu_model": model, "cpus_in_affinity": len(os.sched_getaffinity(0)),
-            "sample": f"{passes} pass(es) over one layer (qkv, o, gate_up, down) of the decode "
-                      f"workload at M in {list(sample_ms)}: {passes * len(sample_ms) * 4} oracle "
-                      f"linears, {nbytes / 1e9:.2f} GB algorithmic, {t:.1f} s of oracle time; "
-                      f"weight prep untimed"}
+    b70 = {"decode": {"value": round(acc[1] / acc[0] / 1e9, 3), "unit": "GB/s"},
+           "prefill": {"value": round(acc[3] / acc[2] / 1e12, 4), "unit": "TOPS"}, **host,
+           "sample": f"{passes} pass(es) over the four Llama-3-70B projections with {nsamp} "
+                     f"output channels each (weights drawn at that size), at M = {m_dec} and on "
+                     f"{psamp} of the {m_pf} token rows: {spent:.1f} s of oracle time; weight "
+                     f"prep untimed"}
+    return decode, prefill, chain, b70
 
 
 def main():
@@ -620,8 +791,16 @@ def main():
 
     if not args.no_cpu_baseline:
         t0 = time.time()
-        out["cpu_baseline"] = cpu_baseline(W, WL, DECODE_MS)
-        log(f"[bench] cpu baseline {time.time() - t0:.1f}s: {out['cpu_baseline']}")
+        decode, prefill, chain, b70 = cpu_baselines(W, WL, DECODE_MS)
+        out["cpu_baseline"] = decode
+        if "prefill" in out:
+            out["prefill"]["cpu_baseline"] = prefill
+        if "chain" in out:
+            out["chain"]["cpu_baseline"] = chain
+        if "llama70b" in out:
+            out["llama70b"]["cpu_baseline"] = b70
+        log(f"[bench] cpu baselines {time.time() - t0:.1f}s: decode {decode}; prefill {prefill}; "
+            f"chain {chain}; llama70b {b70}")
     print(json.dumps(out), flush=True)
 
 
