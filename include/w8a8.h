@@ -60,8 +60,9 @@ typedef enum {
   W8A8_ERROR_HIP = 5            /* the HIP runtime rejected a kernel launch         */
 } w8a8_status_t;
 
-/* Static, NUL-terminated description of a status code. Never NULL. */
-const char* w8a8_status_string(w8a8_status_t status);
+/* Static, NUL-terminated description of a status code (any int: values
+ * that are not a w8a8_status_t give "unknown status"). Never NULL. */
+const char* w8a8_status_string(int status);
 
 /* W8A8_ABI_VERSION of the loaded library. */
 int w8a8_abi_version(void);

@@ -72,7 +72,7 @@ w8a8_status_t validate_gemm(const int8_t* xq, int64_t ldq, const int8_t* wq, int
 
 extern "C" {
 
-const char* w8a8_status_string(w8a8_status_t status) {
+const char* w8a8_status_string(int status) {
   switch (status) {
     case W8A8_SUCCESS: return "success";
     case W8A8_ERROR_INVALID_VALUE: return "invalid value (null pointer, negative size or leading dimension too small)";
