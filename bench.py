@@ -765,6 +765,7 @@ def main():
     if not args.no_prefill:
         p_step, p_gemm, p_launch, p_per, p_stats = run_phase(torch, S, (PREFILL_M,), max(args.steps // 4, 3),
                                                     min(args.warmup, 2), args.detail)
+        clk = gpu_clocks()                   # right after the prefill replays
         ops = sum(2 * PREFILL_M * N * K for _, N, K in S.shapes) * LAYERS
         tops = ops / (p_step * 1e-3) / 1e12
         gtops = ops / (p_gemm * 1e-3) / 1e12
@@ -784,6 +785,15 @@ def main():
                          "launches_per_step": p_launch,
                          "avg_launch_us": round(p_gemm / p_launch * 1e3, 3)},
         }
+        # the same fraction against the peak at the shader clock read right
+        # after the timed replays (the data-sheet peak assumes 2.4 GHz)
+        gfx = clk.get("gfx_per_xcd") or []
+        if gfx:
+            mhz = sum(gfx) / len(gfx)
+            peak_clk = INT8_PEAK_TOPS * mhz / 2400.0
+            out["prefill"]["roofline"]["at_clock"] = {
+                "sclk_mhz": round(mhz, 1), "peak": round(peak_clk, 1),
+                "frac": round(gtops / peak_clk, 4)}
         if p_per:
             out["per_shape_prefill"] = p_per
 

@@ -99,8 +99,9 @@ def test_full_size_linear_sampled(wl_name, proj, N, K, M):
 # ---------------------------------------------------------------------------
 #
 # The launches the benchmark times, compared in full: all 16 Llama-3.1-8B
-# decode (projection, M) pairs and the o and down projections at M = 4096
-# (the prefill kernel at K = 4096 and K = 14336). The int32 accumulators come
+# decode (projection, M) pairs, the four projections at M = 4096 (the prefill
+# kernel's 256 x 256 tile, and 192 x 256 for qkv) and o and down at the
+# chain's 3000 tokens (its 256 x 192 tile). The int32 accumulators come
 # from w8a8_gemm_i32 on the whole problem (the same kernel route as
 # w8a8_gemm at that shape) and every one is compared with the oracle's
 # integer GEMM; every code, scale and bf16 output of w8a8_linear is compared
@@ -109,7 +110,8 @@ def test_full_size_linear_sampled(wl_name, proj, N, K, M):
 # activations at the largest M of the workload and shared by its smaller M.
 
 EVERY_CASES = ([("llama8b_decode", p, N, K, M) for p, N, K in WL.LLAMA31_8B for M in (1, 4, 16, 64)]
-               + [("llama8b_prefill", p, N, K, 4096) for p, N, K in WL.LLAMA31_8B
+               + [("llama8b_prefill", p, N, K, 4096) for p, N, K in WL.LLAMA31_8B]
+               + [("llama8b_chain", p, N, K, 3000) for p, N, K in WL.LLAMA31_8B
                   if p in ("o", "down")])
 
 _prep = {}
