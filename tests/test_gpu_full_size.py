@@ -169,3 +169,42 @@ def test_full_size_every_element(wl_name, proj, N, K, M):
     del acc
     y64, y_ref = O.dequant_epilogue(acc_ref, st_ref, sw_ref)
     check_bf16(host(y), y64, y_ref)
+
+
+# The static-scale linear (one activation scale for every token) on every
+# decode launch the benchmark's static line times, and the Llama-3-70B decode
+# projections o and down at 32 tokens, each compared in full. The static
+# scale is the oracle's min-max calibration on the calibration activations,
+# handed to both sides.
+
+STATIC_CASES = [("llama8b_decode", p, N, K, M) for p, N, K in WL.LLAMA31_8B for M in (1, 4, 16, 64)]
+
+
+@pytest.mark.parametrize("wl_name,proj,N,K,M", STATIC_CASES,
+                         ids=[f"{c[0]}-{c[1]}-M{c[4]}" for c in STATIC_CASES])
+def test_full_size_static_linear_every_element(wl_name, proj, N, K, M):
+    wl = WL.WORKLOADS[wl_name]
+    print(f"\n[static, every element] {wl_name} {proj} M={M} N={N} K={K}", flush=True)
+    s, wq, sw, s_ref, wq_ref, sw_ref = prepared(wl, proj, N, K)
+    out = WL.outlier_channels(K, wl.outlier_frac, wl.name)
+    xcal = WL.activations(max(wl.ms), K, wl.name, proj, 0, outliers=out, mult=wl.outlier_mult)
+    _, S = O.minmax_calibration(O.act_channel_absmax(xcal), s_ref)
+    x = WL.activations(M, K, wl.name, proj, 0, outliers=out, mult=wl.outlier_mult)
+    xd = dev_bf16(x)
+    Sd = torch().tensor([float(S)], dtype=torch().float32, device="cuda")
+    y = W.w8a8_linear_static(xd, s, Sd, wq, sw)
+    xq, st = W.w8a8_quantize_act_static(xd, s, Sd)
+    torch().cuda.synchronize()
+    ref = O.linear_static(x, s_ref, S, wq_ref, sw_ref)
+    np.testing.assert_array_equal(host(st).view(np.uint32), ref["s_tok"].view(np.uint32))
+    np.testing.assert_array_equal(host(xq), ref["xq"])
+    check_bf16(host(y), ref["y64"], ref["y"])
+
+
+B70_CASES = [("llama70b", p, N, K, 32) for p, N, K in WL.LLAMA3_70B if p in ("o", "down")]
+
+
+@pytest.mark.parametrize("wl_name,proj,N,K,M", B70_CASES,
+                         ids=[f"{c[0]}-{c[1]}-M{c[4]}" for c in B70_CASES])
+def test_full_size_70b_decode_every_element(wl_name, proj, N, K, M):
+    test_full_size_every_element(wl_name, proj, N, K, M)
