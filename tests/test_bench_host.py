@@ -110,3 +110,15 @@ def test_clock_readout_parses_amd_smi(monkeypatch):
     out = "note before\n" + json.dumps(doc, indent=2) + "\ntrailing text\n"
     monkeypatch.setattr(sp, "run", lambda *a, **k: types.SimpleNamespace(stdout=out, returncode=0))
     assert bench.gpu_clocks() == {"gfx_per_xcd": [1700, 1701, 1702, 1710], "mem": 2000}
+
+
+def test_oracle_timing_passes_run_until_the_budget():
+    calls = []
+
+    def one_pass():
+        calls.append(1)
+        return 0.4, 10.0
+    t, work, passes = bench._time_passes(one_pass, 1.0)
+    assert passes == 3 and t == pytest.approx(1.2) and work == 30.0
+    host = bench._cpu_host()
+    assert host["kind"] == "oracle" and host["cores"] >= 1 and host["cpus_in_affinity"] >= 1

@@ -57,3 +57,33 @@ def test_noalloc_refuses_oversized_problems():
     y_ref = W.w8a8_linear(x2, s, wq, sw)
     torch().cuda.synchronize()
     np.testing.assert_array_equal(host(y2), host(y_ref))
+
+
+@pytest.mark.parametrize("M,N,K", [(16, 4096, 4096), (64, 1024, 14336)])
+def test_noalloc_linear_under_graph_capture(M, N, K):
+    # the callers it is for: a captured graph replayed with new inputs
+    # written between replays; every replay equals w8a8_linear
+    t = torch()
+    s, wq, sw = _prep(N, K, f"graph{N}x{K}")
+    x = dev_bf16(WL.activations(M, K, "noalloc", "graph", 0))
+    y = t.empty((M, N), dtype=t.bfloat16, device="cuda")
+    side = t.cuda.Stream()
+    side.wait_stream(t.cuda.current_stream())
+    with t.cuda.stream(side):
+        B.w8a8_linear_noalloc(x, s, wq, sw, y=y)          # eager call first
+    t.cuda.current_stream().wait_stream(side)
+    t.cuda.synchronize()
+    g = t.cuda.CUDAGraph()
+    with t.cuda.graph(g):
+        B.w8a8_linear_noalloc(x, s, wq, sw, y=y)
+    t.cuda.synchronize()
+    for replay in range(3):
+        x.copy_(dev_bf16(WL.activations(M, K, "noalloc", "graph", replay + 1)))
+        y.fill_(7.0)
+        t.cuda.synchronize()
+        g.replay()
+        t.cuda.synchronize()
+        got = host(y).copy()
+        want = host(W.w8a8_linear(x, s, wq, sw))
+        t.cuda.synchronize()
+        np.testing.assert_array_equal(got, want, err_msg=f"replay {replay}")
