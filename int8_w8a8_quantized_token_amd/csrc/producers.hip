@@ -146,26 +146,27 @@ struct SqScratch {
   int result;
 };
 
-// sign(S - T) for S the exact sum of squares of the row's values (v holds
-// bf16 values as floats; vectors vi = tid + i BS < nvec) and T > 0 a binary64
-// value with T 2^266 an integer. Called by every thread of the workgroup.
-template <int BS, int NV>
-__device__ __forceinline__ int exact_square_sum_cmp(const float (&v)[NV][8], int nvec, double T,
-                                                 SqScratch* sc) {
+// sign(S - T) for S the exact sum of squares of the row's values and T > 0 a
+// binary64 value with T 2^266 an integer. The values are read back from the
+// row in memory (bf16, nvec vectors of 8); each thread reads the vectors it
+// wrote itself. Called by every thread of the workgroup.
+template <int BS>
+__device__ __forceinline__ int exact_square_sum_cmp(const uint16_t* row, int nvec,
+                                                 double T, SqScratch* sc) {
   const int tid = threadIdx.x;
   for (int k = tid; k < kSqBins; k += BS) sc->bins[k] = 0ull;
   for (int k = tid; k < kLimbs; k += BS) { sc->s[k] = 0u; sc->t[k] = 0u; }
   __syncthreads();
+#pragma unroll 1
+  for (int vi = tid; vi < nvec; vi += BS) {
+    const uint4 raw = *reinterpret_cast<const uint4*>(row + (int64_t)vi * 8);
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    if (tid + i * BS < nvec) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t b = __float_as_uint(v[i][e]) >> 16;   // the value's bf16 bits
-        const uint32_t E = (b >> 7) & 0xFFu, f = b & 0x7Fu;
-        const uint32_t m = E ? (f | 0x80u) : f;
-        if (m) atomicAdd(&sc->bins[E ? E - 1 : 0], (unsigned long long)(m * m));
-      }
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t b = (w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+      const uint32_t E = (b >> 7) & 0xFFu, f = b & 0x7Fu;
+      const uint32_t m = E ? (f | 0x80u) : f;
+      if (m) atomicAdd(&sc->bins[E ? E - 1 : 0], (unsigned long long)(m * m));
     }
   }
   __syncthreads();
@@ -209,13 +210,15 @@ __device__ __forceinline__ int square_sum_cmp_fast(DD ss, double T) {
   return r > bound ? 1 : (r < -bound ? -1 : 2);
 }
 
-// RN32(S / K), ties to even, for S the exact sum of squares of the row. The
-// decisions are the same in every thread (ss is), so either all threads or
-// none take the exact comparison.
-template <int BS, int NV>
-__device__ __forceinline__ float mean_square_rn32(DD ss, int K, const float (&v)[NV][8], int nvec,
-                                                  SqScratch* sc) {
-  const float c = (float)((ss.hi + ss.lo) / (double)K);    // the answer or a neighbour
+// RN32(S / K) where S / K may lie near a binary32 midpoint, from q, an
+// approximation of S / K whose binary32 rounding is RN32(S / K) or a
+// neighbour of it: the two midpoints around that candidate, compared with S as
+// described above.
+template <int BS>
+__device__ __forceinline__ float mean_square_rn32_near(DD ss, double q, int K,
+                                                    const uint16_t* row, int nvec,
+                                                    SqScratch* sc) {
+  const float c = (float)q;
   const uint32_t cb = __float_as_uint(c);
   // the midpoints below and above c; past the largest finite value the
   // overflow threshold 2^128 - 2^103 takes the place of a midpoint
@@ -226,13 +229,42 @@ __device__ __forceinline__ float mean_square_rn32(DD ss, int K, const float (&v)
   int sl = cb != 0u ? square_sum_cmp_fast(ss, tl * (double)K) : 1;
   int su = cb != 0x7F800000u ? square_sum_cmp_fast(ss, tu * (double)K) : -1;
   if (sl == 2 || su == 2) {
-    const int ex = exact_square_sum_cmp<BS, NV>(v, nvec, (sl == 2 ? tl : tu) * (double)K, sc);
+    const int ex = exact_square_sum_cmp<BS>(row, nvec, (sl == 2 ? tl : tu) * (double)K, sc);
     if (sl == 2) sl = ex;
     else su = ex;
   }
   if (sl < 0 || (sl == 0 && (cb & 1u))) return __uint_as_float(cb - 1u);
   if (su > 0 || (su == 0 && (cb & 1u))) return __uint_as_float(cb + 1u);
   return c;
+}
+
+// Whether the binary32 rounding of q = (hi + lo) * RN(1 / K) is RN32(S / K),
+// ties to even, for S the exact sum of squares of the row. q is within 3.01
+// units in its last place of S / K (2^-90 from the double-double, one
+// rounding each for hi + lo, 1 / K and the product). For q in the normal
+// binary32 range its 29 bits below binary32 precision say where q lies
+// between two binary32 values; unless they are within 8 units of the halfway
+// pattern, S / K lies on the same side of the midpoint as q and rounds to
+// RN32(q). The rest (about 2^-25 of rows, plus rows whose mean is not a
+// normal binary32 value) take the comparison with the midpoints.
+__device__ __forceinline__ bool mean_square_clear(DD ss, double q) {
+  const uint32_t low = (uint32_t)(__double_as_longlong(q) & 0x1FFFFFFFll);
+  // evaluated without branches (bitwise, not short-circuit)
+  return (ss.hi == 0.0) |                                 // every square is 0
+         ((q >= 0x1p-126) & (q < 0x1p127) & ((low < 0x10000000u - 8u) | (low > 0x10000000u + 8u)));
+}
+
+// RN32(S / K), ties to even: q's binary32 rounding where mean_square_clear
+// says so, else the comparison with the midpoints. Every thread sees the same
+// ss, so the branch is uniform; the rare case is laid out after the kernel's
+// common path.
+template <int BS>
+__device__ __forceinline__ float mean_square_rn32(DD ss, double q, int K, const uint16_t* row,
+                                                  int nvec, SqScratch* sc) {
+  float ms = (float)q;
+  if (__builtin_expect(!mean_square_clear(ss, q), 0))
+    ms = mean_square_rn32_near<BS>(ss, q, K, row, nvec, sc);
+  return ms;
 }
 
 // ---------------------------------------------------------------------------
@@ -243,7 +275,7 @@ __device__ __forceinline__ float mean_square_rn32(DD ss, int K, const float (&v)
 template <int BS, int NV, bool ADD>
 __global__ __launch_bounds__(BS) void rmsnorm_quantize_kernel(
     uint16_t* __restrict__ h, int64_t ldh, const uint16_t* __restrict__ res, int64_t ldr,
-    const float* __restrict__ g, float eps, int K, int8_t* __restrict__ q, int64_t ldq,
+    const float* __restrict__ g, float eps, int K, double inv_k, int8_t* __restrict__ q, int64_t ldq,
     float* __restrict__ s_tok) {
   __shared__ DD red_dd[BS / kWave];
   __shared__ float red_f[BS / kWave];
@@ -290,7 +322,7 @@ __global__ __launch_bounds__(BS) void rmsnorm_quantize_kernel(
     }
   }
   const DD ss = block_sum_dd<BS>(acc, red_dd);
-  const float ms = mean_square_rn32<BS, NV>(ss, K, v, nvec, &sq);
+  const float ms = mean_square_rn32<BS>(ss, (ss.hi + ss.lo) * inv_k, K, hr, nvec, &sq);
   const float inv = 1.0f / sqrtf(ms + eps);
 
   float amax = 0.0f;
@@ -474,9 +506,10 @@ static hipError_t launch_rmsnorm_bs(uint16_t* h, int64_t ldh, const uint16_t* r,
                                     const float* g, float eps, int64_t M, int64_t K, int8_t* q,
                                     int64_t ldq, float* s_tok, hipStream_t s) {
   const int64_t per = (K / 8 + BS - 1) / BS;
+  const double inv_k = 1.0 / (double)K;                 // correctly rounded
 #define W8A8_RMS(NVV)                                                                             \
   hipLaunchKernelGGL((rmsnorm_quantize_kernel<BS, NVV, ADD>), dim3((unsigned)M), dim3(BS), 0, s, \
-                     h, ldh, r, ldr, g, eps, (int)K, q, ldq, s_tok)
+                     h, ldh, r, ldr, g, eps, (int)K, inv_k, q, ldq, s_tok)
   if (per <= 1) W8A8_RMS(1);
   else if (per <= 2) W8A8_RMS(2);
   else if (per <= 4) W8A8_RMS(4);
