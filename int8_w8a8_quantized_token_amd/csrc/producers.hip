@@ -288,16 +288,21 @@ __global__ __launch_bounds__(BS) void rmsnorm_quantize_kernel(
   // Every load a thread needs (its h, residual and factor vectors) goes out
   // before any arithmetic: one memory round trip per row, not one per vector
   // plus one for the factors after the reduction. Vectors past the row end
-  // load the row's last vector (K >= 16) and are then left out.
+  // load the row's last vector (K >= 16) and are then left out. At 1024
+  // threads (128 registers a lane) with 8 vectors a thread the early factors
+  // would not fit beside the row, so those read them after the reduction.
+  constexpr bool kEarlyG = !(BS == 1024 && NV == 8);
   uint4 hraw[NV], rraw[NV];
-  float gv[NV][8];
+  float gv[kEarlyG ? NV : 1][8];
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int vl = min(tid + i * BS, nvec - 1);
     hraw[i] = *reinterpret_cast<const uint4*>(hr + (int64_t)vl * 8);
     if constexpr (ADD) rraw[i] = *reinterpret_cast<const uint4*>(res + row * ldr + (int64_t)vl * 8);
+    if constexpr (kEarlyG) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) gv[i][e] = g[vl * 8 + e];
+      for (int e = 0; e < 8; ++e) gv[i][e] = g[vl * 8 + e];
+    }
   }
 
   float v[NV][8];
@@ -332,7 +337,10 @@ __global__ __launch_bounds__(BS) void rmsnorm_quantize_kernel(
     if (vi < nvec) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        v[i][e] = (v[i][e] * inv) * gv[i][e];
+        float gi;
+        if constexpr (kEarlyG) gi = gv[i][e];
+        else gi = g[vi * 8 + e];
+        v[i][e] = (v[i][e] * inv) * gi;
         amax = fmaxf(amax, fabsf(v[i][e]));
       }
     }
