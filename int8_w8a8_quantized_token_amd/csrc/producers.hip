@@ -396,9 +396,10 @@ __device__ __forceinline__ float silu_mul_fast(float g, float u, bool& ok) {
   const float m = q * u;
   const float a = fabsf(m);
   const int lo = (int)(__float_as_uint(m) & 0xFFFFu);
-  const bool clear = lo > 0x8000 + 16 || lo < 0x8000 - 16;
-  ok = fabsf(g) <= 80.0f &&
-       (g == 0.0f || u == 0.0f || (a >= 0x1p-120f && a < 0x1p120f && clear));
+  // bitwise, not short-circuit: the compiler would branch per value
+  const bool clear = (lo > 0x8000 + 16) | (lo < 0x8000 - 16);
+  ok = (fabsf(g) <= 80.0f) &
+       ((g == 0.0f) | (u == 0.0f) | ((a >= 0x1p-120f) & (a < 0x1p120f) & clear));
   return __uint_as_float(f32_to_bf16_rne(m) << 16);
 }
 
