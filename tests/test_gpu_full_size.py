@@ -8,8 +8,9 @@ a sample of token rows (codes and scales), and the int32 accumulators (of
 w8a8_gemm_i32 on the whole problem) and bf16 outputs on the sampled rows x
 sampled columns. Rows of both quantizations are independent of each other,
 so a sampled row is checked exactly. Properties that hold at any size are
-checked on the whole output. The second test below compares every element
-of the decode launches and of two prefill launches.
+checked on the whole output. The tests further below compare every element
+of every one of those launches: the Llama-3.1-8B decode, prefill and chain
+projections and the Llama-3-70B projections.
 """
 import numpy as np
 import pytest
@@ -100,8 +101,8 @@ def test_full_size_linear_sampled(wl_name, proj, N, K, M):
 #
 # The launches the benchmark times, compared in full: all 16 Llama-3.1-8B
 # decode (projection, M) pairs, the four projections at M = 4096 (the prefill
-# kernel's 256 x 256 tile, and 192 x 256 for qkv) and o and down at the
-# chain's 3000 tokens (its 256 x 192 tile). The int32 accumulators come
+# kernel's 256 x 256 tile, and 192 x 256 for qkv) and at the chain's 3000
+# tokens (256 x 192 tiles for o and down). The int32 accumulators come
 # from w8a8_gemm_i32 on the whole problem (the same kernel route as
 # w8a8_gemm at that shape) and every one is compared with the oracle's
 # integer GEMM; every code, scale and bf16 output of w8a8_linear is compared
@@ -111,8 +112,7 @@ def test_full_size_linear_sampled(wl_name, proj, N, K, M):
 
 EVERY_CASES = ([("llama8b_decode", p, N, K, M) for p, N, K in WL.LLAMA31_8B for M in (1, 4, 16, 64)]
                + [("llama8b_prefill", p, N, K, 4096) for p, N, K in WL.LLAMA31_8B]
-               + [("llama8b_chain", p, N, K, 3000) for p, N, K in WL.LLAMA31_8B
-                  if p in ("o", "down")])
+               + [("llama8b_chain", p, N, K, 3000) for p, N, K in WL.LLAMA31_8B])
 
 _prep = {}
 
@@ -201,10 +201,12 @@ def test_full_size_static_linear_every_element(wl_name, proj, N, K, M):
     check_bf16(host(y), ref["y64"], ref["y"])
 
 
-B70_CASES = [("llama70b", p, N, K, 32) for p, N, K in WL.LLAMA3_70B if p in ("o", "down")]
+# The four Llama-3-70B projections at both of the workload's token counts:
+# 32 (mid kernel) and 2048 (prefill kernel), every element.
+B70_CASES = [("llama70b", p, N, K, M) for p, N, K in WL.LLAMA3_70B for M in (32, 2048)]
 
 
 @pytest.mark.parametrize("wl_name,proj,N,K,M", B70_CASES,
                          ids=[f"{c[0]}-{c[1]}-M{c[4]}" for c in B70_CASES])
-def test_full_size_70b_decode_every_element(wl_name, proj, N, K, M):
+def test_full_size_70b_every_element(wl_name, proj, N, K, M):
     test_full_size_every_element(wl_name, proj, N, K, M)
