@@ -257,8 +257,37 @@ def gpu_clocks():
         return {"error": f"{type(e).__name__}: {str(e)[:120]}"}
 
 
-def run_phase(torch, S, ms, steps, warmup, detail):
-    """Times one step (all layers, projections, token counts) and its GEMMs."""
+def clocks_under_load(torch, graph, ms_per_replay, seconds=3.0):
+    """The clocks (as gpu_clocks reports them) read while `graph` replays back
+    to back for about `seconds`: a side thread reads them a third of the way
+    in, while the main thread keeps the queue full."""
+    import threading
+    res = {}
+
+    def sample():
+        time.sleep(seconds / 3)
+        res["clk"] = gpu_clocks()
+
+    t = threading.Thread(target=sample)
+    t.start()
+    end = time.monotonic() + seconds
+    n = 0
+    while n < 2 or time.monotonic() < end:
+        graph.replay()
+        n += 1
+        if n % 8 == 0:                    # keep at most a few replays queued ahead
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    t.join()
+    out = dict(res.get("clk", {"error": "no reading"}))
+    out["replays"] = n
+    out["replay_ms"] = round(ms_per_replay, 3)
+    return out
+
+
+def run_phase(torch, S, ms, steps, warmup, detail, on_gemm_graph=None):
+    """Times one step (all layers, projections, token counts) and its GEMMs;
+    on_gemm_graph(graph, ms) runs on the timed GEMM graph afterwards."""
     def step():
         for M in ms:
             for layer in range(LAYERS):
@@ -278,6 +307,8 @@ def run_phase(torch, S, ms, steps, warmup, detail):
     ms_step, step_stats = time_graph(torch, g_step, steps, warmup, stats=True)
     g_gemm = capture(torch, gemms)
     ms_gemm = time_graph(torch, g_gemm, steps, warmup)
+    if on_gemm_graph is not None:
+        on_gemm_graph(g_gemm, ms_gemm)
     launches = len(ms) * LAYERS * len(S.shapes)
     per = {}
     if detail:
@@ -763,9 +794,10 @@ def main():
         out["llama70b"] = run_70b(torch, W, WL, args)
 
     if not args.no_prefill:
-        p_step, p_gemm, p_launch, p_per, p_stats = run_phase(torch, S, (PREFILL_M,), max(args.steps // 4, 3),
-                                                    min(args.warmup, 2), args.detail)
-        clk = gpu_clocks()                   # right after the prefill replays
+        clk = {}
+        p_step, p_gemm, p_launch, p_per, p_stats = run_phase(
+            torch, S, (PREFILL_M,), max(args.steps // 4, 3), min(args.warmup, 2), args.detail,
+            on_gemm_graph=lambda g, t: clk.update(clocks_under_load(torch, g, t)))
         ops = sum(2 * PREFILL_M * N * K for _, N, K in S.shapes) * LAYERS
         tops = ops / (p_step * 1e-3) / 1e12
         gtops = ops / (p_gemm * 1e-3) / 1e12
@@ -785,15 +817,19 @@ def main():
                          "launches_per_step": p_launch,
                          "avg_launch_us": round(p_gemm / p_launch * 1e3, 3)},
         }
-        # the same fraction against the peak at the shader clock read right
-        # after the timed replays (the data-sheet peak assumes 2.4 GHz)
+        # the same fraction against the peak at the shader clock read while
+        # the GEMM graph replays back to back (the data-sheet peak assumes
+        # 2.4 GHz; under this load the chip runs slower, power-limited)
         gfx = clk.get("gfx_per_xcd") or []
         if gfx:
             mhz = sum(gfx) / len(gfx)
             peak_clk = INT8_PEAK_TOPS * mhz / 2400.0
             out["prefill"]["roofline"]["at_clock"] = {
                 "sclk_mhz": round(mhz, 1), "peak": round(peak_clk, 1),
-                "frac": round(gtops / peak_clk, 4)}
+                "frac": round(gtops / peak_clk, 4),
+                "read": f"amd-smi during {clk['replays']} back-to-back replays of the GEMM graph"}
+        else:
+            out["prefill"]["roofline"]["at_clock"] = {"error": clk.get("error", "no reading")}
         if p_per:
             out["per_shape_prefill"] = p_per
 

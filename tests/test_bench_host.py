@@ -122,3 +122,24 @@ def test_oracle_timing_passes_run_until_the_budget():
     assert passes == 3 and t == pytest.approx(1.2) and work == 30.0
     host = bench._cpu_host()
     assert host["kind"] == "oracle" and host["cores"] >= 1 and host["cpus_in_affinity"] >= 1
+
+
+def test_clocks_are_read_while_the_graph_replays(monkeypatch):
+    state = {"replays": 0, "at_read": None, "running": True}
+
+    class Graph:
+        def replay(self):
+            state["replays"] += 1
+            import time
+            time.sleep(0.002)              # a replay keeps the device busy a while
+
+    def clocks():
+        state["at_read"] = state["replays"]
+        return {"gfx_per_xcd": [1900] * 8, "mem": 2000}
+
+    fake_torch = types.SimpleNamespace(cuda=types.SimpleNamespace(synchronize=lambda: None))
+    monkeypatch.setattr(bench, "gpu_clocks", clocks)
+    out = bench.clocks_under_load(fake_torch, Graph(), 2.0, seconds=0.3)
+    assert out["gfx_per_xcd"] == [1900] * 8 and out["replays"] == state["replays"]
+    # read after the load started and before it ended
+    assert 0 < state["at_read"] < state["replays"]
