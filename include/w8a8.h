@@ -36,6 +36,11 @@
  *       ld * element_size a multiple of 16. Outputs with N columns (y, acc)
  *       need only element alignment and any ld >= N.
  *     Violations give W8A8_ERROR_UNSUPPORTED (K) or W8A8_ERROR_MISALIGNED.
+ *   - Token and output-channel counts (M, N, and the rows of the quantizers
+ *     and producers) are at most 2^22 - 1, and M * N at most 2^37; the
+ *     calibration reductions and the residual add take up to 2^31 - 65536
+ *     rows; GPTQ takes at most 2^19 output channels. Larger sizes give
+ *     W8A8_ERROR_UNSUPPORTED.
  *   - Thread-safe: calls on different streams may run concurrently.
  */
 #ifndef W8A8_H
@@ -55,7 +60,7 @@ typedef enum {
   W8A8_SUCCESS = 0,
   W8A8_ERROR_INVALID_VALUE = 1, /* NULL required pointer, negative size, ld too small */
   W8A8_ERROR_MISALIGNED = 2,    /* pointer or row stride below required alignment   */
-  W8A8_ERROR_UNSUPPORTED = 3,   /* K % 16 != 0, K > 131072, size overflow           */
+  W8A8_ERROR_UNSUPPORTED = 3,   /* K % 16 != 0, K > 131072, size past the limits  */
   W8A8_ERROR_WORKSPACE = 4,     /* workspace NULL or smaller than required          */
   W8A8_ERROR_HIP = 5            /* the HIP runtime rejected a kernel launch         */
 } w8a8_status_t;

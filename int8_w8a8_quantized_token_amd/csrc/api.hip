@@ -15,7 +15,16 @@ constexpr int64_t kMaxK = 131072;  // 128 * 128 * K stays below 2^31
 constexpr int64_t kMinBins = W8A8_QUANT_LEVELS;
 constexpr int64_t kMaxBins = 8192;
 constexpr int64_t kMaxProducerK = 65536;   // 8 vectors of 8 per thread at 1024 threads
-constexpr int64_t kMaxDim = INT32_MAX;
+// Sizes of the kernels that stride over rows (calibration, histogram,
+// residual add) and of vectors: below 2^31 - 65536, so that any count
+// rounded up to a block and every index formed from it fit in int.
+constexpr int64_t kMaxDim = (int64_t)INT32_MAX - 65535;
+// Tokens and output channels of the row and GEMM kernels: one workgroup
+// of up to 1024 threads per row, or output tiles of at least 192 x 256 with
+// 512 threads, so at most 2^22 - 1 rows and 2^37 outputs keep every grid
+// dimension within 2^32 work-items (2^37 bf16 outputs exceed HBM anyway).
+constexpr int64_t kMaxRows = (int64_t(1) << 22) - 1;
+constexpr int64_t kMaxOutputs = int64_t(1) << 37;
 
 inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -49,7 +58,8 @@ w8a8_status_t check_vector(const void* p) {
 w8a8_status_t check_dims(int64_t rows, int64_t K, int64_t N = 1) {
   if (rows < 0 || K < 0 || N < 0) return W8A8_ERROR_INVALID_VALUE;
   if (K == 0) return W8A8_ERROR_INVALID_VALUE;
-  if (K % 16 != 0 || K > kMaxK || rows > kMaxDim || N > kMaxDim) return W8A8_ERROR_UNSUPPORTED;
+  if (K % 16 != 0 || K > kMaxK || rows > kMaxRows || N > kMaxRows) return W8A8_ERROR_UNSUPPORTED;
+  if (rows * N > kMaxOutputs) return W8A8_ERROR_UNSUPPORTED;
   return W8A8_SUCCESS;
 }
 
@@ -124,7 +134,7 @@ w8a8_status_t w8a8_gemm_i32(const int8_t* xq, int64_t ldq, const int8_t* wq, int
 }
 
 size_t w8a8_linear_workspace_bytes(int64_t M, int64_t K) {
-  if (M <= 0 || K <= 0 || M > kMaxDim || K > kMaxK) return 0;
+  if (M <= 0 || K <= 0 || M > kMaxRows || K > kMaxK) return 0;
   return align256((size_t)M * (size_t)K) + align256((size_t)M * sizeof(float));
 }
 
@@ -344,6 +354,7 @@ w8a8_status_t w8a8_residual_add(uint16_t* h, int64_t ldh, const uint16_t* r, int
 // GPTQ -------------------------------------------------------------------
 
 constexpr int64_t kGptqMaxK = 32768;   // K x K binary64 factor: 8 GiB at the limit
+constexpr int64_t kGptqMaxN = int64_t(1) << 19;   // column-update grid: N / 16 rows of blocks
 constexpr int64_t kGptqPanel = 64;
 
 w8a8_status_t w8a8_gptq_hessian(const uint16_t* x, int64_t ldx, const float* smooth, int64_t n,
@@ -377,7 +388,7 @@ w8a8_status_t w8a8_gptq_factor(const double* H, int64_t K, double damp, double* 
 }
 
 size_t w8a8_gptq_quantize_workspace_bytes(int64_t N, int64_t K) {
-  if (N <= 0 || K <= 0 || K > kGptqMaxK || N > kMaxDim) return 0;
+  if (N <= 0 || K <= 0 || K > kGptqMaxK || N > kGptqMaxN) return 0;
   return align256((size_t)N * (size_t)K * sizeof(double)) +
          align256((size_t)N * kGptqPanel * sizeof(double));
 }
@@ -387,7 +398,7 @@ w8a8_status_t w8a8_gptq_quantize(const uint16_t* w, int64_t ldw, const float* sm
                                  float* s_chan, void* workspace, size_t workspace_bytes,
                                  hipStream_t stream) {
   W8A8_TRY(check_dims(N, K));
-  if (K > kGptqMaxK) return W8A8_ERROR_UNSUPPORTED;
+  if (K > kGptqMaxK || N > kGptqMaxN) return W8A8_ERROR_UNSUPPORTED;
   if (N == 0) return W8A8_SUCCESS;
   W8A8_TRY(check_matrix(w, ldw, N, K, 2));
   W8A8_TRY(check_matrix(wq, ldwq, N, K, 1));

@@ -106,7 +106,7 @@ int main() {
   // fake, never dereferenced addresses: A aligned, MIS 8-byte aligned only
   char* const A = reinterpret_cast<char*>(0x10000);
   char* const MIS = A + 8;
-  const int64_t BIG = INT64_MAX, I32 = INT32_MAX;
+  const int64_t BIG = INT64_MAX, I32 = INT32_MAX, ROWS = (int64_t(1) << 22) - 1;
   auto u16 = [](char* p) { return reinterpret_cast<uint16_t*>(p); };
   auto i8 = [](char* p) { return reinterpret_cast<int8_t*>(p); };
   auto f32 = [](char* p) { return reinterpret_cast<float*>(p); };
@@ -123,7 +123,10 @@ int main() {
   EXPECT(w8a8_abi_version(), W8A8_ABI_VERSION);
   EXPECT(w8a8_linear_workspace_bytes(-1, 16) == 0, 1);
   EXPECT(w8a8_linear_workspace_bytes(BIG, BIG) == 0, 1);
-  EXPECT(w8a8_linear_workspace_bytes(I32, 131072) > 0, 1);
+  EXPECT(w8a8_linear_workspace_bytes(ROWS, 131072) > 0, 1);
+  EXPECT(w8a8_linear_workspace_bytes(ROWS + 1, 131072) == 0, 1);
+  EXPECT(w8a8_gptq_quantize_workspace_bytes(1 << 19, 16) > 0, 1);
+  EXPECT(w8a8_gptq_quantize_workspace_bytes((1 << 19) + 1, 16) == 0, 1);
   EXPECT(w8a8_gptq_factor_workspace_bytes(-5) == 0, 1);
   EXPECT(w8a8_gptq_factor_workspace_bytes(BIG) == 0, 1);
   EXPECT(w8a8_gptq_quantize_workspace_bytes(BIG, BIG) == 0, 1);
@@ -148,6 +151,11 @@ int main() {
   EXPECT(w8a8_gemm_i32(i8(A), 64, i8(A), 64, 4, 10, 64, i32(A + 2), 10, 0), MISAL);
   EXPECT(w8a8_gemm_i32(i8(A), 64, i8(A), 64, 4, 8, 64, i32(A), 6, 0), INV);
   EXPECT(w8a8_gemm_i32(i8(A), 64, i8(A), 64, I32, I32, 64, i32(A), BIG, 0), UNS);
+  EXPECT(w8a8_gemm(i8(A), 16, f32(A), i8(A), 16, f32(A), 1, ROWS + 1, 16, u16(A), ROWS + 1, 0),
+         UNS);                                             // N past the channel bound
+  EXPECT(w8a8_gemm(i8(A), 16, f32(A), i8(A), 16, f32(A), ROWS, ROWS, 16, u16(A), ROWS, 0),
+         UNS);                                             // M * N past 2^37 outputs
+  EXPECT(w8a8_quantize_act(u16(A), 16, nullptr, ROWS + 1, 16, i8(A), 16, f32(A), 0), UNS);
 
   // linears
   EXPECT(w8a8_linear(u16(A), 4096, nullptr, i8(A), 4096, f32(A), 16, 4096, 4096, u16(A), 4096,
@@ -162,8 +170,10 @@ int main() {
                             u16(A), 4096, A, 1 << 20, 0), INV);
   EXPECT(w8a8_linear_noalloc(u16(A), 4096, nullptr, i8(A), 4096, f32(A), 2048, 4096, 4096, u16(A),
                              4096, 0), WS);
-  EXPECT(w8a8_linear_noalloc(u16(A), 131072, nullptr, i8(A), 131072, f32(A), I32, 16, 131072,
-                             u16(A), 16, 0), WS);
+  EXPECT(w8a8_linear_noalloc(u16(A), 131072, nullptr, i8(A), 131072, f32(A), ROWS, 16,
+                             131072, u16(A), 16, 0), WS);
+  EXPECT(w8a8_linear_noalloc(u16(A), 131072, nullptr, i8(A), 131072, f32(A), ROWS + 1, 16,
+                             131072, u16(A), 16, 0), UNS);  // M past the row bound
   EXPECT(w8a8_linear_noalloc(nullptr, 4096, nullptr, i8(A), 4096, f32(A), 16, 4096, 4096, u16(A),
                              4096, 0), INV);
 
