@@ -281,6 +281,80 @@ MUTANTS = {
     "gptq_factor_lower": ("gptq_factor", _gptq_factor_lower),
 }
 
+# --- further plausible mistakes -------------------------------------------
+
+def _residual_subtracts(h_bf16, r_bf16):               # h - r instead of h + r
+    return O.round_to_bf16(O.bf16_to_f32(h_bf16) - O.bf16_to_f32(r_bf16))
+
+
+def _linear_drops_smoothing(x_bf16, smooth, wq, s_chan):
+    xq, s_tok = O.quantize_act(x_bf16, None)
+    acc = O.gemm_i32(xq, wq)
+    y64, y = O.dequant_epilogue(acc, s_tok, s_chan)
+    return {"xq": xq, "s_tok": s_tok, "acc": acc, "y64": y64, "y": y}
+
+
+def _linear_static_drops_smoothing(x_bf16, smooth, scale, wq, s_chan):
+    xq, s_tok = O.quantize_act_static(x_bf16, None, scale)
+    acc = O.gemm_i32(xq, wq)
+    y64, y = O.dequant_epilogue(acc, s_tok, s_chan)
+    return {"xq": xq, "s_tok": s_tok, "acc": acc, "y64": y64, "y": y}
+
+
+def _entropy_last_minimum(hist, amax, levels=O.QUANT_LEVELS):   # ties go to the largest i
+    kl = O.entropy_kl(hist, levels)
+    bins = len(hist)
+    sub = kl[levels:]
+    i_best = levels + int(len(sub) - 1 - np.argmin(sub[::-1]))
+    w = F32(F32(amax) / F32(bins))
+    T = F32(F32(i_best) * w)
+    return i_best, T, F32(T / F32(O.QMAX)), kl
+
+
+def _hessian_not_doubled(x_bf16, smooth=None):          # X'^T X' without the 2
+    xs = O.smooth_activations(O.bf16_to_f32(x_bf16), smooth).astype(np.float64)
+    return xs.T @ xs
+
+
+def _hessian_unsmoothed(x_bf16, smooth=None):           # raw activations
+    xs = O.bf16_to_f32(x_bf16).astype(np.float64)
+    return 2.0 * (xs.T @ xs)
+
+
+def _act_absmax_signed(x_bf16):                         # max x instead of max |x|
+    return np.max(O.bf16_to_f32(x_bf16), axis=0).astype(F32)
+
+
+def _silu_sign_slip(gu_bf16):                           # g / (1 + e^g)
+    x = O.bf16_to_f32(gu_bf16).astype(np.float64)
+    inter = x.shape[1] // 2
+    g, u = x[:, :inter], x[:, inter:2 * inter]
+    with np.errstate(over="ignore"):
+        m = (g / (1.0 + np.exp(g))) * u
+    return O.round_to_bf16(m)
+
+
+def _ratio_truncates(num, den):                         # toward zero, not nearest
+    q = O._round_ratio_f32(num, den)
+    exact = num / den
+    if float(q) > exact and q > 0:
+        return np.nextafter(q, F32(0))
+    return q
+
+
+MUTANTS.update({
+    "residual_add_subtracts": ("residual_add", _residual_subtracts),
+    "linear_drops_smoothing": ("linear", _linear_drops_smoothing),
+    "linear_static_drops_smoothing": ("linear_static", _linear_static_drops_smoothing),
+    "entropy_last_minimum": ("entropy_calibration", _entropy_last_minimum),
+    "hessian_not_doubled": ("gptq_hessian", _hessian_not_doubled),
+    "hessian_unsmoothed": ("gptq_hessian", _hessian_unsmoothed),
+    "act_absmax_signed": ("act_channel_absmax", _act_absmax_signed),
+    "silu_sign_slip": ("silu_mul", _silu_sign_slip),
+    "mean_square_truncates": ("_round_ratio_f32", _ratio_truncates),
+})
+
+
 PINS = [getattr(P, n) for n in dir(P)
         if n.startswith("test_") and callable(getattr(P, n))]
 
@@ -296,3 +370,4 @@ def test_some_pin_catches(name, monkeypatch):
         except Exception:                         # assertion or shape error
             caught.append(pin.__name__)
     assert caught, f"mutant {name} survived every pin"
+

@@ -594,6 +594,23 @@ def test_linear_static_composition():
             assert int(out["y"][m, n]) == bf16_bits_of(y)
 
 
+def test_linear_static_smoothing_by_hand():
+    # x' = x / s with power-of-two factors is exact; with S = 1/16 the codes
+    # are x' * 16 clamped: x = [8, -4, 2, 1, 3], s = [2, 4, 1/2, 1, 1/4]
+    # gives x' = [4, -1, 4, 1, 12] and codes [64, -16, 64, 16, 127 (192
+    # clamped)]; against the unsmoothed x the codes would be [127, -64, 32,
+    # 16, 48]. One weight row of ones adds the codes.
+    x = O.round_to_bf16(np.array([[8, -4, 2, 1, 3]], F32))
+    s = np.array([2, 4, 0.5, 1, 0.25], F32)
+    S = F32(1 / 16)
+    wq = np.ones((1, 5), np.int8)
+    out = O.linear_static(x, s, S, wq, np.array([1.0], F32))
+    assert out["xq"].tolist() == [[64, -16, 64, 16, 127]]
+    assert out["acc"].tolist() == [[255]]
+    # 255 / 16 = 15.9375 = 0b1111.1111 has 8 significant bits: exact in bf16
+    assert float(O.bf16_to_f32(out["y"])[0, 0]) == 15.9375
+
+
 # ---------------------------------------------------------------------------
 # fused producers (RMSNorm + quantize, SiLU-gated product + quantize)
 # ---------------------------------------------------------------------------
@@ -884,6 +901,19 @@ def test_gptq_factor_and_hessian():
     H0 = H.copy(); H0[5, :] = 0; H0[:, 5] = 0
     U0 = O.gptq_factor(H0)
     assert np.all(np.isfinite(U0))
+
+
+def test_gptq_hessian_of_smoothed_activations():
+    # with power-of-two smoothing factors x / s is exact, so the Hessian of
+    # the smoothed activations is the raw one scaled entry by entry by
+    # 1 / (s_i s_j), exactly
+    r = np.random.default_rng(32)
+    x = O.round_to_bf16(r.standard_normal((40, 16)).astype(F32))
+    s = (2.0 ** r.integers(-3, 4, 16)).astype(F32)
+    H_raw = O.gptq_hessian(x)
+    H_s = O.gptq_hessian(x, s)
+    assert not np.array_equal(H_s, H_raw)
+    np.testing.assert_array_equal(H_s, H_raw / np.outer(s, s).astype(np.float64))
 
 
 def test_gptq_lowers_output_error_against_rtn():
