@@ -248,3 +248,50 @@ def test_chain_config_full_size_sampled_rows(chain_params):
     np.testing.assert_array_equal(out[rows], want)
     h = O.bf16_to_f32(out)
     assert np.all(np.isfinite(h))
+
+
+# Shapes that reach every (threads, vectors per thread) instance of the two
+# producers that the launch rule can pick (256 threads with 1, 2 or 4
+# vectors of 8 per thread, 512 with 4 or 8, 1024 with 1, 2, 4 or 8; the
+# fixed shapes here and in the tests above), plus seeded random shapes. Every code and scale is compared with the oracle's.
+_FIXED_SHAPES = [(700, 6144), (520, 16384), (530, 30000), (520, 40000), (600, 1024),
+                 (2, 160), (511, 12000), (300, 20000)]
+_r = np.random.default_rng(20240)
+PRODUCER_SHAPES = _FIXED_SHAPES + [(int(_r.integers(1, 700)), 16 * int(_r.integers(1, 1300)))
+                                   for _ in range(4)]
+
+
+def _threads_and_vectors(M, K):
+    """The producers' launch rule, restated for the test ids."""
+    bs = 1024 if M <= 512 else (512 if K > 8192 else 256)
+    while bs < 1024 and -(-(K // 8) // bs) > 8:
+        bs *= 2
+    per = -(-(K // 8) // bs)
+    return bs, 1 if per <= 1 else 2 if per <= 2 else 4 if per <= 4 else 8
+
+
+@pytest.mark.parametrize("M,K", PRODUCER_SHAPES,
+                         ids=[f"M{m}-K{k}-bs{_threads_and_vectors(m, k)[0]}"
+                              f"-nv{_threads_and_vectors(m, k)[1]}" for m, k in PRODUCER_SHAPES])
+def test_producers_every_launch_shape(M, K):
+    print(f"\n[producers] M={M} K={K} {_threads_and_vectors(M, K)}", flush=True)
+    h = act(M, K, f"shape-h-{M}-{K}")
+    res = WL.activations(M, K, "producers", f"shape-r-{M}-{K}", frac=0.0, mult=1.0)
+    s = np.exp(WL.rng("shape-s", K).uniform(-1, 1, K)).astype(F32)
+    g = O.fold_gamma(gamma_with_outliers(K, "shape"), s)
+    for add in (False, True):
+        q_ref, s_ref, h_ref = O.rmsnorm_quantize(h, res if add else None, g, EPS)
+        d_h = dev_bf16(h)
+        xq, st = W.w8a8_rmsnorm_quantize(d_h, dev(g), EPS,
+                                         residual=dev_bf16(res) if add else None)
+        torch().cuda.synchronize()
+        np.testing.assert_array_equal(host(d_h), h_ref)
+        np.testing.assert_array_equal(host(st).view(np.uint32), s_ref.view(np.uint32))
+        np.testing.assert_array_equal(host(xq), q_ref)
+    gu = WL.activations(M, 2 * K, "producers", f"shape-gu-{M}-{K}", frac=0.01, mult=20.0)
+    for smooth in (None, s):
+        q_ref, s_ref = O.silu_mul_quantize(gu, smooth)
+        xq, st = W.w8a8_silu_mul_quantize(dev_bf16(gu), dev(smooth) if smooth is not None else None)
+        torch().cuda.synchronize()
+        np.testing.assert_array_equal(host(st).view(np.uint32), s_ref.view(np.uint32))
+        np.testing.assert_array_equal(host(xq), q_ref)
