@@ -30,6 +30,8 @@
  *     surface at the caller's next synchronization, as for any HIP kernel.
  *   - No C++ exception crosses this interface.
  *   - M == 0 or N == 0 is a valid empty call: W8A8_SUCCESS, nothing launched.
+ *   - Activation, weight and scale values are finite; a non-finite input
+ *     value gives unspecified codes, scales and outputs (never a fault).
  *   - Requirements shared by the entry points that read int8/bf16 rows:
  *       K % 16 == 0, 0 < K <= 131072 (so |acc| <= 128*128*K stays in int32);
  *       pointers to K-long rows (x, xq, w, wq) 16-byte aligned, with

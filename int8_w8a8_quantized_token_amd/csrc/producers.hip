@@ -136,9 +136,11 @@ __device__ __forceinline__ uint4 pack8_bf16(const float (&v)[8]) {
 
 // Number of bins of exact_square_sum_cmp: a bf16 value with biased exponent E
 // is m 2^(e) with integer significand m < 256 and e = max(E, 1) - 134, so its
-// square is m^2 4^(max(E, 1) - 1) 2^-266 and squares fall into 254 bins.
-constexpr int kSqBins = 254;
-constexpr int kLimbs = 18;           // 32-bit limbs of S 2^266 < 2^539
+// square is m^2 4^(max(E, 1) - 1) 2^-266 and finite squares fall into bins
+// 0 .. 253; bin 254 takes E = 255 (inf, NaN), whose rows have no defined
+// result but must not index past the array.
+constexpr int kSqBins = 255;
+constexpr int kLimbs = 18;           // 32-bit limbs of S 2^266 < 2^539 (< 2^541 with bin 254)
 
 struct SqScratch {
   unsigned long long bins[kSqBins];  // sum of m^2 per exponent (< 65536 * 2^16)
