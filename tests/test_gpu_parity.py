@@ -37,10 +37,13 @@ def i8(shape, *key):
 
 QA_SHAPES = [(1, 16), (2, 48), (3, 64), (15, 4096 + 16), (16, 4096), (17, 2048),
              (63, 512), (64, 14336), (65, 4096), (127, 1040), (255, 256), (4, 40960),
-             # many rows: several rows per workgroup, ragged M and channel tails,
-             # and K beyond the register-resident limit
+             # many rows (256 or 512 threads per row), ragged M and channel
+             # tails, and K beyond the register-resident limit
              (513, 4096), (1024, 4096 + 16), (1100, 14336), (2049, 2048), (8200, 64),
              (600, 40960),
+             # the two remaining (threads, vectors per thread) instances:
+             # 1024 threads x 4 vectors and 512 threads x 8 vectors
+             (100, 20000), (700, 24000),
              # few rows longer than 1024 threads hold in registers (read twice),
              # up to the largest K the library accepts
              (5, 65536 + 16), (1, 131072)]
@@ -108,8 +111,9 @@ def test_quantize_act_crafted_rows_many(K):
 
 @pytest.mark.parametrize("M", [16, 600])
 def test_quantize_act_smoothing_edges(M):
-    # smoothing factors outside [2^-20, 2^20] and activations below 2^-80 or
-    # exactly zero take the division; the rest the reciprocal form
+    # smoothing factors at and beyond 2^-20 and 2^20 (up to 2^-30 and 2^30),
+    # activations below 2^-80 and exact zeros, and a row of tiny values only:
+    # quotients far from 1 through the smoothing division and the code step
     K = 1024
     r = WL.rng("smooth-edges", M, K)
     smooth = np.exp(r.uniform(-3, 3, K)).astype(F32)
